@@ -1,0 +1,237 @@
+// Host side of the C-ABI: plan arithmetic, workspace layout, argument checks
+// and the three launches of a call.  Owns no device memory and keeps no state.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include "mla_verify_internal.h"
+
+using namespace mlav;
+
+namespace {
+
+constexpr uint64_t kAlign = 256;
+
+uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+const PlanImpl* as_impl(const mla_verify_plan_t* plan) {
+  if (!plan) return nullptr;
+  const PlanImpl* impl = reinterpret_cast<const PlanImpl*>(plan);
+  if (impl->magic != kPlanMagic || impl->abi_version != MLA_VERIFY_ABI_VERSION) return nullptr;
+  return impl;
+}
+
+bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+mla_verify_status_t check_args(const PlanImpl& pl, const mla_verify_args_t* a, const void* ws,
+                               size_t ws_bytes) {
+  if (!a) return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  const mla_verify_config_t& c = pl.cfg;
+  if (a->batch_size < 0 || a->batch_size > c.max_batch) return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  if (!isfinite(a->sm_scale)) return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  if (!a->q || !a->kv_pool || !a->qo_indptr || !a->kv_indptr || !a->kv_indices ||
+      !a->out_cache_loc || !a->custom_mask || !a->mask_indptr || !a->out)
+    return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  // 16-byte vector loads of q / pool rows and 16-byte stores of out
+  if (!aligned(a->q, 16) || a->q_stride_tok <= 0 || a->q_stride_head <= 0 ||
+      a->q_stride_tok % 8 || a->q_stride_head % 8)
+    return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  if (!aligned(a->kv_pool, 16) || a->kv_row_stride < kDqk || a->kv_row_stride % 8 ||
+      a->num_slots <= 0)
+    return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  if (!aligned(a->out, 16) || a->out_stride_tok <= 0 || a->out_stride_head <= 0 ||
+      a->out_stride_tok % 4 || a->out_stride_head % 4)
+    return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  if (a->lse && (!aligned(a->lse, 4) || a->lse_stride_tok <= 0))
+    return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  if (!aligned(a->qo_indptr, 4) || !aligned(a->kv_indptr, 4) || !aligned(a->mask_indptr, 4))
+    return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  if (!aligned(a->kv_indices, c.kv_indices_dtype == MLA_VERIFY_I64 ? 8 : 4) ||
+      !aligned(a->out_cache_loc, c.out_cache_loc_dtype == MLA_VERIFY_I64 ? 8 : 4))
+    return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  if (!ws || !aligned(ws, kAlign)) return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < pl.layout.total_bytes) return MLA_VERIFY_ERR_WORKSPACE_TOO_SMALL;
+  return MLA_VERIFY_OK;
+}
+
+KernelParams make_params(const PlanImpl& pl, const mla_verify_args_t* a, void* ws) {
+  KernelParams p;
+  memset(&p, 0, sizeof(p));
+  const mla_verify_config_t& c = pl.cfg;
+  const mla_verify_layout_t& l = pl.layout;
+  unsigned char* base = static_cast<unsigned char*>(ws);
+  p.batch = a->batch_size;
+  p.num_heads = c.num_heads;
+  p.sm_scale_log2 = a->sm_scale * 1.4426950408889634f;
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.q_stride_tok = a->q_stride_tok;
+  p.q_stride_head = a->q_stride_head;
+  p.kv_pool = static_cast<const uint16_t*>(a->kv_pool);
+  p.kv_row_stride = a->kv_row_stride;
+  p.num_slots = a->num_slots;
+  p.qo_indptr = a->qo_indptr;
+  p.kv_indptr = a->kv_indptr;
+  p.kv_indices = a->kv_indices;
+  p.out_cache_loc = a->out_cache_loc;
+  p.custom_mask = a->custom_mask;
+  p.mask_indptr = a->mask_indptr;
+  p.out = a->out;
+  p.out_stride_tok = a->out_stride_tok;
+  p.out_stride_head = a->out_stride_head;
+  p.lse = a->lse;
+  p.lse_stride_tok = a->lse_stride_tok;
+  p.kv_idx64 = c.kv_indices_dtype == MLA_VERIFY_I64;
+  p.ocl_idx64 = c.out_cache_loc_dtype == MLA_VERIFY_I64;
+  p.max_q_tokens = c.max_q_tokens;
+  p.max_tree_nodes = c.max_tree_nodes;
+  p.max_kv_tokens = c.max_kv_tokens;
+  p.target_items = l.target_items;
+  p.item_capacity = l.item_capacity;
+  p.flags = c.flags;
+  p.hdr = reinterpret_cast<WsHeader*>(base + l.header_offset);
+  p.req = reinterpret_cast<int32_t*>(base + l.request_offset);
+  p.anc = reinterpret_cast<uint64_t*>(base + l.anc_offset);
+  p.items = reinterpret_cast<int32_t*>(base + l.items_offset);
+  p.part_o = reinterpret_cast<float*>(base + l.partial_o_offset);
+  p.part_ml = reinterpret_cast<float*>(base + l.partial_ml_offset);
+  p.trace = (c.flags & MLA_VERIFY_FLAG_TRACE_KEYS) ? reinterpret_cast<int64_t*>(base + l.trace_offset)
+                                                   : nullptr;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_verify_abi_version(void) { return MLA_VERIFY_ABI_VERSION; }
+
+const char* mla_verify_status_string(mla_verify_status_t s) {
+  switch (s) {
+    case MLA_VERIFY_OK: return "ok";
+    case MLA_VERIFY_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MLA_VERIFY_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MLA_VERIFY_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MLA_VERIFY_ERR_LAUNCH: return "kernel launch failed";
+    case MLA_VERIFY_ERR_BAD_PLAN: return "not a plan made by mla_verify_plan";
+  }
+  return "unknown status";
+}
+
+mla_verify_status_t mla_verify_plan(const mla_verify_config_t* cfg, mla_verify_plan_t* plan) {
+  if (!cfg || !plan) return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  const mla_verify_config_t c = *cfg;
+  if (c.num_heads < 1 || c.max_batch < 1 || c.max_q_tokens < 1 || c.max_tree_nodes < 1 ||
+      c.max_kv_tokens < 0 || c.target_items < 0 || c.cu_count < 0)
+    return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  if ((c.kv_indices_dtype != MLA_VERIFY_I32 && c.kv_indices_dtype != MLA_VERIFY_I64) ||
+      (c.out_cache_loc_dtype != MLA_VERIFY_I32 && c.out_cache_loc_dtype != MLA_VERIFY_I64))
+    return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  if (c.flags & ~(uint32_t)MLA_VERIFY_FLAG_TRACE_KEYS) return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  for (int i = 0; i < 7; ++i)
+    if (c.reserved[i]) return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  if (c.max_tree_nodes > MLA_VERIFY_MAX_TREE_NODES || c.max_batch > kMaxBatch)
+    return MLA_VERIFY_ERR_UNSUPPORTED;
+  // int32 key and row indices inside the kernels
+  if (c.max_kv_tokens > (int64_t)INT32_MAX - c.max_q_tokens) return MLA_VERIFY_ERR_UNSUPPORTED;
+  const int64_t max_rows = (int64_t)c.max_q_tokens * c.num_heads;
+  if (max_rows > INT32_MAX / 2) return MLA_VERIFY_ERR_UNSUPPORTED;
+
+  int32_t cu = c.cu_count;
+  if (cu == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
+      return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  }
+  const int32_t target = c.target_items > 0 ? c.target_items : cu;
+
+  PlanImpl impl;
+  memset(&impl, 0, sizeof(impl));
+  impl.magic = kPlanMagic;
+  impl.abi_version = MLA_VERIFY_ABI_VERSION;
+  impl.cfg = c;
+  impl.cfg.cu_count = cu;
+  mla_verify_layout_t& l = impl.layout;
+  // every request adds at most one partly filled key range per row block
+  const int64_t row_blocks_bound = (max_rows + kRowsPerItem - 1) / kRowsPerItem + c.max_batch;
+  const int64_t capacity = (int64_t)target + row_blocks_bound;
+  if (capacity > INT32_MAX / 2) return MLA_VERIFY_ERR_UNSUPPORTED;
+  l.item_capacity = (int32_t)capacity;
+  l.rows_per_item = kRowsPerItem;
+  l.keys_per_tile = kKeysPerTile;
+  l.target_items = target;
+  l.partial_grid = (int32_t)capacity;
+  l.merge_grid = (int32_t)max_rows;
+
+  uint64_t off = 0;
+  l.header_offset = off;
+  off = align_up(off + sizeof(WsHeader));
+  l.request_offset = off;
+  off = align_up(off + (uint64_t)c.max_batch * 8 * sizeof(int32_t));
+  l.anc_offset = off;
+  off = align_up(off + (uint64_t)c.max_q_tokens * sizeof(uint64_t));
+  l.items_offset = off;
+  off = align_up(off + (uint64_t)capacity * 8 * sizeof(int32_t));
+  l.partial_o_offset = off;
+  off = align_up(off + (uint64_t)capacity * kRowsPerItem * kDv * sizeof(float));
+  l.partial_ml_offset = off;
+  off = align_up(off + (uint64_t)capacity * kRowsPerItem * 2 * sizeof(float));
+  l.trace_offset = 0;
+  if (c.flags & MLA_VERIFY_FLAG_TRACE_KEYS) {
+    l.trace_offset = off;
+    off = align_up(off + ((uint64_t)c.max_kv_tokens + c.max_q_tokens) * sizeof(int64_t));
+  }
+  l.total_bytes = off;
+
+  memset(plan, 0, sizeof(*plan));
+  memcpy(plan, &impl, sizeof(impl));
+  return MLA_VERIFY_OK;
+}
+
+mla_verify_status_t mla_verify_workspace_size(const mla_verify_plan_t* plan, size_t* bytes) {
+  const PlanImpl* pl = as_impl(plan);
+  if (!pl) return MLA_VERIFY_ERR_BAD_PLAN;
+  if (!bytes) return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  *bytes = (size_t)pl->layout.total_bytes;
+  return MLA_VERIFY_OK;
+}
+
+mla_verify_status_t mla_verify_workspace_layout(const mla_verify_plan_t* plan,
+                                                mla_verify_layout_t* layout) {
+  const PlanImpl* pl = as_impl(plan);
+  if (!pl) return MLA_VERIFY_ERR_BAD_PLAN;
+  if (!layout) return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  *layout = pl->layout;
+  return MLA_VERIFY_OK;
+}
+
+mla_verify_status_t mla_verify_run_phase(const mla_verify_plan_t* plan, const mla_verify_args_t* args,
+                                         void* workspace, size_t workspace_bytes, void* stream,
+                                         int32_t phase) {
+  const PlanImpl* pl = as_impl(plan);
+  if (!pl) return MLA_VERIFY_ERR_BAD_PLAN;
+  if (phase < 0 || phase > 2) return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  const mla_verify_status_t st = check_args(*pl, args, workspace, workspace_bytes);
+  if (st != MLA_VERIFY_OK) return st;
+  const KernelParams p = make_params(*pl, args, workspace);
+  int rc = 0;
+  if (phase == 0) rc = launch_meta(p, pl->layout, stream);
+  else if (phase == 1) rc = launch_partial(p, pl->layout, stream);
+  else rc = launch_merge(p, pl->layout, stream);
+  return rc == 0 ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;
+}
+
+mla_verify_status_t mla_verify_run(const mla_verify_plan_t* plan, const mla_verify_args_t* args,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  const PlanImpl* pl = as_impl(plan);
+  if (!pl) return MLA_VERIFY_ERR_BAD_PLAN;
+  const mla_verify_status_t st = check_args(*pl, args, workspace, workspace_bytes);
+  if (st != MLA_VERIFY_OK) return st;
+  const KernelParams p = make_params(*pl, args, workspace);
+  if (launch_meta(p, pl->layout, stream) != 0) return MLA_VERIFY_ERR_LAUNCH;
+  if (launch_partial(p, pl->layout, stream) != 0) return MLA_VERIFY_ERR_LAUNCH;
+  if (launch_merge(p, pl->layout, stream) != 0) return MLA_VERIFY_ERR_LAUNCH;
+  return MLA_VERIFY_OK;
+}
+
+}  // extern "C"

@@ -41,8 +41,11 @@ BF16_NAN = np.uint16(0xFFFF)
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bf16 (nearest, ties to even); returns uint16 bits."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    if not np.isfinite(x).all():
+        raise ValueError("only finite values are rounded here")
+    # finite inputs: |u| <= 0x7F7FFFFF (+ sign) so the sum cannot wrap in 32 bits
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return rounded.astype(np.uint16)
 
 
@@ -251,3 +254,91 @@ def segmented(replay: int = 0, seed: Optional[int] = None) -> Instance:
     trees = rng.integers(sp["tree_lo"], sp["tree_hi"] + 1, size=sp["batch"]).tolist()
     return _build(f"segmented_r{replay}", s, sp["num_heads"], sp["num_slots"], prefix, trees,
                   "random", 0.0, rng)
+
+
+def segmented_pool(seed: int = 2999, num_slots: Optional[int] = None,
+                   chunk_rows: int = 1 << 17, threads: int = 8) -> np.ndarray:
+    """A fully populated bf16 pool [num_slots, 576] (N(0,1) rows) for replays
+    that rewrite only metadata and queries between calls.  Chunk c of
+    ``chunk_rows`` rows is drawn from child c of SeedSequence(seed), so the
+    bits do not depend on the thread count."""
+    from concurrent.futures import ThreadPoolExecutor
+    n = SEGMENTED["num_slots"] if num_slots is None else num_slots
+    pool = np.empty((n, D_QK), dtype=np.uint16)
+    starts = list(range(0, n, chunk_rows))
+    kids = np.random.SeedSequence(seed).spawn(len(starts))
+
+    def fill(c):
+        r0 = starts[c]
+        r1 = min(n, r0 + chunk_rows)
+        rng = np.random.default_rng(kids[c])
+        pool[r0:r1] = f32_to_bf16_bits(rng.standard_normal((r1 - r0, D_QK), dtype=np.float32))
+
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        list(ex.map(fill, range(len(starts))))
+    return pool
+
+
+@dataclasses.dataclass
+class Replay:
+    """Metadata and queries of one call over a fixed, fully populated pool."""
+    seed: int
+    num_heads: int
+    num_slots: int
+    q: np.ndarray
+    qo_indptr: np.ndarray
+    kv_indptr: np.ndarray
+    kv_indices: np.ndarray
+    out_cache_loc: np.ndarray
+    custom_mask: np.ndarray
+    mask_indptr: np.ndarray
+    parents: List[List[int]]
+    prefix_lens: List[int]
+    tree_sizes: List[int]
+    sm_scale: float = float(SM_SCALE)
+
+    @property
+    def batch(self) -> int:
+        return len(self.prefix_lens)
+
+    @property
+    def total_q(self) -> int:
+        return int(self.qo_indptr[-1])
+
+    @property
+    def total_kv(self) -> int:
+        return int(self.kv_indptr[-1])
+
+
+def segmented_replay(replay: int, num_slots: Optional[int] = None) -> Replay:
+    """Replay ``replay`` of the segmented batch (seed 2000 + replay): fresh sizes,
+    trees, slot placement and queries; rows come from ``segmented_pool``."""
+    s = 2000 + replay
+    rng = np.random.default_rng(s)
+    sp = SEGMENTED
+    n_slots = sp["num_slots"] if num_slots is None else num_slots
+    prefix = rng.integers(sp["prefix_lo"], sp["prefix_hi"] + 1, size=sp["batch"]).tolist()
+    trees = rng.integers(sp["tree_lo"], sp["tree_hi"] + 1, size=sp["batch"]).tolist()
+    perm = rng.permutation(n_slots).astype(np.int64)
+    parents = [random_parents(rng, t) for t in trees]
+    total_q = int(sum(trees))
+    q = f32_to_bf16_bits(rng.standard_normal((total_q, sp["num_heads"], D_QK), dtype=np.float32))
+    b = sp["batch"]
+    qo = np.zeros(b + 1, np.int32)
+    kv = np.zeros(b + 1, np.int32)
+    mi = np.zeros(b + 1, np.int32)
+    qo[1:] = np.cumsum(trees)
+    kv[1:] = np.cumsum(prefix)
+    mi[1:] = np.cumsum([t * t for t in trees])
+    kv_indices = np.empty(int(kv[-1]), np.int32)
+    ocl = np.empty(total_q, np.int64)
+    off = 0
+    for i, (p, t) in enumerate(zip(prefix, trees)):
+        kv_indices[kv[i]:kv[i + 1]] = perm[off:off + p]
+        ocl[qo[i]:qo[i + 1]] = perm[off + p:off + p + t]
+        off += p + t
+    mask = np.concatenate([ancestor_or_self_mask(par).reshape(-1) for par in parents])
+    return Replay(seed=s, num_heads=sp["num_heads"], num_slots=n_slots, q=q, qo_indptr=qo,
+                  kv_indptr=kv, kv_indices=kv_indices, out_cache_loc=ocl,
+                  custom_mask=mask.astype(np.uint8), mask_indptr=mi, parents=parents,
+                  prefix_lens=prefix, tree_sizes=trees)
