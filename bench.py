@@ -1,0 +1,236 @@
+"""Benchmark of tree-masked MLA verify attention on one MI355X.
+
+Workload (one step = one verify call = metadata build + split partials + merge):
+1 request, 91,136-token prefix scattered over a 1,048,576-slot page_size=1 pool,
+32-node random draft tree, H = 8 heads, 576-wide bf16 latent (V = first 512
+dims), 1% of prefix rows scaled by 8, fp32 output + LSE.  Inputs are seeded
+synthetic data resident in HBM before the timed region.
+
+Prints one JSON line: value = effective KV bandwidth (bytes of the gathered
+latent rows / time per call) in GB/s; us_per_call beside it; the roofline of the
+split-partial kernel (MFMA-bound at 256 query rows: algorithmic flops / its
+average duration from HIP events on the launch stream); and the CPU oracle
+timed on this host on the same call.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs/call + effective KV GB/s & %roofline, 91k-prefix 32-node tree verify"
+WORKLOAD = "p91136_t32"
+PEAK_MFMA_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
+KERNEL_SRC = os.path.join(ROOT, "speculative_decoding_mla_page_amd", "csrc", "mla_verify_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mla_verify_partial_p91136_t32_traffic.txt")
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic(inst):
+    """Algorithmic flops and KV bytes of one call: every query row (node x head)
+    takes 576 + 512 multiply-adds per visible-or-not key of its request."""
+    flops = 0
+    kv_bytes = 0
+    for p, t in zip(inst.prefix_lens, inst.tree_sizes):
+        n = p + t
+        flops += 2 * (t * inst.num_heads) * n * (576 + 512)
+        kv_bytes += n * 1152
+    return flops, kv_bytes
+
+
+def read_traffic(launch_keys: int):
+    """HBM bytes per partial-kernel launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    txt = open(TRAFFIC_FILE).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*(\w+)", txt)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def cpu_baseline(inst, kv_bytes, budget_s: float = 20.0):
+    """The oracle, as it stands, on the same call; repeated while under budget."""
+    import numpy as np
+    from oracle import mla_verify_ref as R
+    try:
+        import threadpoolctl
+        np.ones((4, 4)) @ np.ones((4, 4))
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    view = inst.pool_view()
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 3 and (time.perf_counter() - t_start) < budget_s:
+        t0 = time.perf_counter()
+        R.mla_verify_reference(inst.q, view, inst.qo_indptr, inst.kv_indptr, inst.kv_indices,
+                               inst.out_cache_loc, inst.custom_mask, inst.mask_indptr,
+                               inst.num_heads, inst.sm_scale)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    return {"value": kv_bytes / t / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"whole {WORKLOAD} call (all 32 nodes x 8 heads over 91,168 keys), "
+                      f"median of {len(times)} runs, numpy fp64 with {threads} BLAS threads on "
+                      f"{cpu_model()}",
+            "us_per_call": t * 1e6}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-calls", type=int, default=20,
+                    help="extra calls each preceded by a 1 GiB cache scrub (reported, not the value)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from speculative_decoding_mla_page_amd import binding as B
+    from speculative_decoding_mla_page_amd.device import DeviceInputs, Verifier
+    from workloads import gen
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU"}), flush=True)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    inst = gen.config(WORKLOAD)
+    flops, kv_bytes = algorithmic(inst)
+    di = DeviceInputs(inst)
+    ver = Verifier.for_inputs(di)
+    out, lse = di.alloc_outputs()
+    a = ver.args(di, out, lse)
+    stream = torch.cuda.current_stream()
+    sp = int(stream.cuda_stream)
+
+    def step(evs=None):
+        if evs is None:
+            B.run(ver.plan, a, ver.workspace, sp)
+            return
+        evs[0].record(stream)
+        B.run_phase(ver.plan, a, ver.workspace, B.PHASE_META, sp)
+        evs[1].record(stream)
+        B.run_phase(ver.plan, a, ver.workspace, B.PHASE_PARTIAL, sp)
+        evs[2].record(stream)
+        B.run_phase(ver.plan, a, ver.workspace, B.PHASE_MERGE, sp)
+        evs[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if ver.error_word() != 0:
+        raise RuntimeError(f"device error word {ver.error_word():#x}")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    meta_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    part_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    merge_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    call_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    span_ms = evs[0][0].elapsed_time(evs[-1][3])
+    ms_per_step = wall * 1e3 / args.steps
+
+    # cold calls: scrub the 256 MB Infinity Cache and L2 with a 1 GiB write first
+    cold_us = None
+    if args.cold_calls > 0:
+        scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        ce = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.cold_calls)]
+        for i in range(args.cold_calls):
+            scrub.fill_(float(i))
+            ce[i][0].record(stream)
+            step()
+            ce[i][1].record(stream)
+        torch.cuda.synchronize()
+        cold_us = float(np.median([e[0].elapsed_time(e[1]) for e in ce]) * 1e3)
+        del scrub
+
+    # reference numbers: the same call checked for the device error word
+    if ver.error_word() != 0:
+        raise RuntimeError(f"device error word {ver.error_word():#x}")
+
+    us_call = float(np.mean(call_ms) * 1e3)
+    part_us = float(np.mean(part_ms) * 1e3)
+    achieved_tflops = flops / (part_us * 1e-6) / 1e12
+    traffic = read_traffic(inst.total_kv)
+    result = {
+        "metric": METRIC,
+        "value": kv_bytes / (us_call * 1e-6) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "1 request, 91,136-token prefix, 32-node random tree, H=8, "
+                               "576-d bf16 latent (V = first 512), 1% outlier rows x8, "
+                               "page_size=1 pool of 1,048,576 slots, fp32 out + LSE",
+                   "name": WORKLOAD, "batch": 1, "prefix_tokens": 91136, "tree_nodes": 32,
+                   "heads": 8, "query_rows": 256, "keys": inst.total_kv + inst.total_q},
+        "us_per_call": us_call,
+        "us_per_call_p10_p90": [float(np.percentile(call_ms, 10) * 1e3),
+                                float(np.percentile(call_ms, 90) * 1e3)],
+        "us_per_call_cold": cold_us,
+        "kernel_us": {"meta": float(np.mean(meta_ms) * 1e3), "partial": part_us,
+                      "merge": float(np.mean(merge_ms) * 1e3)},
+        "event_span_ms_per_step": span_ms / args.steps,
+        "tflops_per_call": flops / (us_call * 1e-6) / 1e12,
+        "algorithmic": {"flops": flops, "kv_bytes": kv_bytes},
+        "roofline": {"bound": "mfma", "achieved": achieved_tflops,
+                     "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved_tflops / PEAK_MFMA_BF16_TFLOPS,
+                     "traffic": traffic, "kernel": "partial_kernel",
+                     "kernel_source_sha256_16": kernel_hash()},
+        "roofline_call": {"t_roof_us": max(kv_bytes / (PEAK_HBM_GBS * 1e9),
+                                           flops / (PEAK_MFMA_BF16_TFLOPS * 1e12)) * 1e6,
+                          "frac": max(kv_bytes / (PEAK_HBM_GBS * 1e9),
+                                      flops / (PEAK_MFMA_BF16_TFLOPS * 1e12)) / (us_call * 1e-6)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inst, kv_bytes)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
