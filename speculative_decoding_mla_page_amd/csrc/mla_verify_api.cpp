@@ -160,7 +160,8 @@ mla_verify_status_t mla_verify_plan(const mla_verify_config_t* cfg, mla_verify_p
   l.rows_per_item = kRowsPerItem;
   l.keys_per_tile = kKeysPerTile;
   l.target_items = target;
-  l.partial_grid = (int32_t)capacity;
+  // the partial kernel maps workgroups to items XCD by XCD (8 XCDs): whole groups of 8
+  l.partial_grid = (int32_t)((capacity + 7) / 8 * 8);
   l.merge_grid = (int32_t)max_rows;
 
   uint64_t off = 0;

@@ -11,8 +11,11 @@ constexpr int kDqk = MLA_VERIFY_D_QK;      // 576
 constexpr int kDv = MLA_VERIFY_D_V;        // 512
 constexpr int kKeysPerTile = 32;           // keys staged in LDS per inner step
 constexpr int kWaves = 4;                  // waves per workgroup (one per SIMD)
-constexpr int kRowsPerWave = 16;           // query rows owned by one wave
-constexpr int kRowsPerItem = kWaves * kRowsPerWave;  // 64 rows per work item
+constexpr int kRowTiles = 1;               // 16-row MFMA tiles of query rows per wave
+constexpr int kRowsPerWave = 16 * kRowTiles;
+constexpr int kRowsPerItem = kWaves * kRowsPerWave;  // query rows per work item
+constexpr int kStages = 4;                 // key tiles in flight through LDS
+constexpr int kIdxKeys = 1024;             // slots staged per index block (32 tiles)
 constexpr int kPartialThreads = kWaves * 64;
 constexpr int kMetaThreads = 256;
 constexpr int kMergeThreads = 128;         // 128 lanes x 4 dims = 512

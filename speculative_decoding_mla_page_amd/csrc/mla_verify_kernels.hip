@@ -32,22 +32,23 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// LDS layout of one staged key tile (kKeysPerTile keys):
-//   s_k : key-major copy, row = key, 576 bf16 + 16 bytes of padding, read as the
-//         A operand of S^T = K.Q^T (16 contiguous bytes of one key per lane).
-//   s_vt: dim-major copy of V = dims [0,512): row = dim, 4 key groups x 8 keys
-//         + 16 bytes of padding, read as the A operand of O^T = V^T.P^T.
-constexpr int kKStride = kDqk * 2 + 16;                  // 1168 bytes
-constexpr int kVtStride = kKeysPerTile * 2 + 16;         // 80 bytes
-constexpr int kSkBytes = kKeysPerTile * kKStride;        // 37376
-constexpr int kSvtBytes = kDv * kVtStride;               // 40960
+// LDS layout of one staged tile of kKeysPerTile keys (one pipeline stage):
+//   V part   : key k's dims [0, 512) at k * kVStride; the 16 spare bytes per row
+//              put the 16 keys an MFMA operand read touches in distinct banks.
+//   rope part: key k's dims [512, 576) at kVPart + k * 128, its eight 16-byte
+//              units stored at unit ^ (k & 7) (the rows of eight keys are
+//              written by one 1 KB direct-to-LDS load, so they cannot be padded).
+constexpr int kVStride = kDv * 2 + 16;                   // 1040 bytes
+constexpr int kVPart = kKeysPerTile * kVStride;          // 33280
+constexpr int kStageBytes = kVPart + kKeysPerTile * 128; // 37376
+constexpr int kTilesPerIdx = kIdxKeys / kKeysPerTile;    // 32
+constexpr float kRescaleSlack = 8.f;  // rescale O only when a row max grows by > 2^8
 
 // Key order inside a 32-key tile for the PV product.  Lane group g (lanes
 // 16g..16g+15) feeds keys kappa(g, 0..7) = {4g..4g+3, 16+4g..16+4g+3} as its
 // eight K-dimension slots; these are exactly the keys whose scores the same
 // lanes hold in the S^T accumulators (rows 4g+i of each 16-key output tile),
 // so P moves from the softmax to the PV operand without any data exchange.
-__device__ __forceinline__ int kappa(int g, int j) { return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4); }
 
 __device__ __forceinline__ int64_t load_index(const void* base, int64_t i, int is64) {
   return is64 ? reinterpret_cast<const int64_t*>(base)[i]
@@ -191,191 +192,302 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// split partial: one workgroup (4 waves x 16 query rows) per work item
+// split partial: one workgroup (4 waves x kRowsPerWave query rows) per work item
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t perm_lo(uint32_t x, uint32_t y) {
-  return __builtin_amdgcn_perm(y, x, 0x05040100u);  // lo16(x) | lo16(y) << 16
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define MLAV_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
+
+// Wait until at most `n` vector-memory operations of this wave are still in
+// flight (direct-to-LDS loads complete in issue order and count here), finish
+// this wave's LDS operations, then meet the other waves.  The memory clobber
+// keeps the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void wait_vm_barrier(int n) {
+  if (n >= 18) asm volatile("s_waitcnt vmcnt(18) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if (n >= 9) asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
-__device__ __forceinline__ uint32_t perm_hi(uint32_t x, uint32_t y) {
-  return __builtin_amdgcn_perm(y, x, 0x07060302u);  // hi16(x) | hi16(y) << 16
-}
+static_assert(kStages == 4, "wait_vm_barrier covers up to two tiles (18 loads) in flight");
 
 __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char s_k[kSkBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char s_vt[kSvtBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char s_tiles[kStages * kStageBytes];
+  __shared__ int32_t s_idx[2][kIdxKeys];
 
-  const int item = blockIdx.x;
-  if (item >= p.hdr->n_items) return;
+  // Work items of one key range sit on one XCD: workgroup b is dispatched to
+  // XCD b % 8, so XCD x gets the contiguous items [x*per, (x+1)*per) and the
+  // row blocks that share a key range share that XCD's L2.
+  const int n_items = p.hdr->n_items;
+  const int per_xcd = (n_items + 7) >> 3;
+  const int bid = blockIdx.x;
+  if ((bid >> 3) >= per_xcd) return;
+  const int item = (bid & 7) * per_xcd + (bid >> 3);
+  if (item >= n_items) return;
+
   const int32_t* e = p.items + (size_t)item * 8;
-  const int b = e[IT_B], rb = e[IT_RB], key0 = e[IT_KEY0], key1 = e[IT_KEY1];
+  const int rb = e[IT_RB], key0 = e[IT_KEY0], key1 = e[IT_KEY1];
   const int nrows = e[IT_NROWS], row0 = e[IT_ROW0];
-  const int32_t* rq = p.req + b * 8;
+  const int32_t* rq = p.req + e[IT_B] * 8;
   const int P = rq[RQ_P], q0 = rq[RQ_Q0], kv0 = rq[RQ_KV0];
   const int H = p.num_heads;
+  const int ntiles = (key1 - key0 + kKeysPerTile - 1) / kKeysPerTile;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
 
-  // this lane's query row: rows are (node, head) pairs, heads fastest
-  const int r_local = wave * kRowsPerWave + n;
-  const bool row_ok = r_local < nrows;
-  const int r = row0 + r_local;
-  const int tok = q0 + r / H, head = r % H;
-  bf16x8 qf[kDqk / 32];
-  {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
+  // query rows of this lane, one per 16-row tile rt; rows are (node, head)
+  // pairs with heads fastest
+  bf16x8 qf[kRowTiles][kDqk / 32];
+  uint64_t anc[kRowTiles];
+  bool row_ok[kRowTiles];
+#pragma unroll
+  for (int rt = 0; rt < kRowTiles; ++rt) {
+    const int r_local = wave * kRowsPerWave + 16 * rt + n;
+    row_ok[rt] = r_local < nrows;
+    const int r = row0 + r_local;
+    const int tok = q0 + r / H, head = r % H;
     const uint16_t* qrow = p.q + (int64_t)tok * p.q_stride_tok + (int64_t)head * p.q_stride_head;
 #pragma unroll
     for (int ks = 0; ks < kDqk / 32; ++ks) {
-      u32x4 v = row_ok ? *reinterpret_cast<const u32x4*>(qrow + ks * 32 + g * 8) : zero;
-      qf[ks] = __builtin_bit_cast(bf16x8, v);
+      u32x4 v = row_ok[rt] ? *reinterpret_cast<const u32x4*>(qrow + ks * 32 + g * 8)
+                           : u32x4{0u, 0u, 0u, 0u};
+      qf[rt][ks] = __builtin_bit_cast(bf16x8, v);
     }
+    anc[rt] = row_ok[rt] ? p.anc[tok] : 0ull;
   }
-  const uint64_t anc = row_ok ? p.anc[tok] : 0ull;
   const bool wave_active = wave * kRowsPerWave < nrows;
   const bool trace = (p.flags & MLA_VERIFY_FLAG_TRACE_KEYS) && rb == 0;
   const int64_t trace0 = (int64_t)kv0 + q0;
 
-  f32x4 o[kDv / 16];
-#pragma unroll
-  for (int dt = 0; dt < kDv / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  // ---- slots: blocks of kIdxKeys keys staged in LDS (double buffered) ----
+  // load_idx only issues the index loads; store_idx (a block later) checks
+  // the slots, records the trace and writes them to LDS, so the loads never
+  // hold up the tile pipeline.
   bool poison = false;
-
-  // gather assignment: wave w loads keys kappa(w, 0..7), lane = 16-byte column
-  // of dims [0, 512); every thread also loads one 16-byte piece of the rope dims
-  const int dg = lane;
-  const int kr = tid >> 3, rg = tid & 7;
-  u32x4 gm[8];
-  u32x4 gr;
-
-  auto gather = [&](int t0) {
+  uint32_t idx_lo[kIdxKeys / kPartialThreads], idx_hi[kIdxKeys / kPartialThreads];
+  auto load_idx = [&](int blk) {
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int j = t0 + kappa(wave, jj);
-      const int64_t slot = key_slot(p, j, key1, P, kv0, q0);
-      const bool ok = slot >= 0 && slot < p.num_slots;
-      if (!ok && j < key1) poison = true;
-      gm[jj] = ok ? *reinterpret_cast<const u32x4*>(p.kv_pool + slot * p.kv_row_stride + dg * 8)
-                  : u32x4{0u, 0u, 0u, 0u};
-    }
-    const int j = t0 + kr;
-    const int64_t slot = key_slot(p, j, key1, P, kv0, q0);
-    const bool ok = slot >= 0 && slot < p.num_slots;
-    if (!ok && j < key1) poison = true;
-    gr = ok ? *reinterpret_cast<const u32x4*>(p.kv_pool + slot * p.kv_row_stride + kDv + rg * 8)
-            : u32x4{0u, 0u, 0u, 0u};
-    if (trace && rg == 0 && j < key1) p.trace[trace0 + j] = slot;
-  };
-
-  auto stage = [&]() {
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj)
-      *reinterpret_cast<u32x4*>(s_k + kappa(wave, jj) * kKStride + dg * 16) = gm[jj];
-    *reinterpret_cast<u32x4*>(s_k + kr * kKStride + kDv * 2 + rg * 16) = gr;
-    // 8 keys x 8 dims -> 8 dims x 8 keys
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const int w = d >> 1;
-      u32x4 v;
-      if ((d & 1) == 0) {
-        v[0] = perm_lo(gm[0][w], gm[1][w]);
-        v[1] = perm_lo(gm[2][w], gm[3][w]);
-        v[2] = perm_lo(gm[4][w], gm[5][w]);
-        v[3] = perm_lo(gm[6][w], gm[7][w]);
-      } else {
-        v[0] = perm_hi(gm[0][w], gm[1][w]);
-        v[1] = perm_hi(gm[2][w], gm[3][w]);
-        v[2] = perm_hi(gm[4][w], gm[5][w]);
-        v[3] = perm_hi(gm[6][w], gm[7][w]);
-      }
-      *reinterpret_cast<u32x4*>(s_vt + (dg * 8 + d) * kVtStride + wave * 16) = v;
-    }
-  };
-
-  gather(key0);
-  for (int t0 = key0; t0 < key1; t0 += kKeysPerTile) {
-    __syncthreads();  // previous tile's LDS reads are done
-    stage();
-    __syncthreads();
-    if (t0 + kKeysPerTile < key1) gather(t0 + kKeysPerTile);
-
-    if (wave_active) {
-      // S^T tile: 32 keys x 16 rows, two 16-key MFMA tiles, K-dim 576
-      f32x4 s[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const unsigned char* kp = s_k + (16 * kt + n) * kKStride + g * 16;
-#pragma unroll
-        for (int ks = 0; ks < kDqk / 32; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + ks * 64);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], acc, 0, 0, 0);
+    for (int i = 0; i < kIdxKeys / kPartialThreads; ++i) {
+      const int j = key0 + blk * kIdxKeys + tid + kPartialThreads * i;
+      const bool prefix = j < P;
+      const void* base = prefix ? p.kv_indices : p.out_cache_loc;
+      const int64_t at = prefix ? (int64_t)kv0 + j : (int64_t)q0 + (j - P);
+      const bool wide = prefix ? p.kv_idx64 : p.ocl_idx64;
+      uint32_t lo = 0, hi = 0;
+      if (j < key1) {
+        if (wide) {
+          const uint32_t* w = reinterpret_cast<const uint32_t*>(base) + 2 * at;
+          lo = w[0];
+          hi = w[1];
+        } else {
+          lo = reinterpret_cast<const uint32_t*>(base)[at];
         }
-        s[kt] = acc;
       }
-      // scale to base-2 units, mask the range tail and invisible tree keys
-      float mx = -INFINITY;
+      idx_lo[i] = lo;
+      idx_hi[i] = hi;
+    }
+  };
+  auto store_idx = [&](int blk) {
+#pragma unroll
+    for (int i = 0; i < kIdxKeys / kPartialThreads; ++i) {
+      const int j = key0 + blk * kIdxKeys + tid + kPartialThreads * i;
+      const bool wide = j < P ? p.kv_idx64 : p.ocl_idx64;
+      const int64_t slot = wide ? (int64_t)(((uint64_t)idx_hi[i] << 32) | idx_lo[i])
+                                : (int64_t)(int32_t)idx_lo[i];
+      int32_t v = 0;
+      if (j < key1) {
+        if (trace) p.trace[trace0 + j] = slot;
+        if (slot >= 0 && slot < p.num_slots) v = (int32_t)slot;
+        else poison = true;   // read slot 0 instead; the whole item's rows become NaN
+      }
+      s_idx[blk & 1][tid + kPartialThreads * i] = v;
+    }
+  };
+
+  // ---- direct-to-LDS gather of tile t: 9 loads of 1 KB per wave ----
+  // wave w fetches keys 8w..8w+7 of the tile: one load per key for dims
+  // [0,512) (lane = 16-byte unit) and one load for the eight rope rows.  Keys
+  // past the range end re-read the range's last key (finite data, masked).
+  auto issue = [&](int t) {
+    unsigned char* stage = s_tiles + (t % kStages) * kStageBytes;
+    const int blk_first = key0 + (t / kTilesPerIdx) * kIdxKeys;
+    const int32_t* idx = s_idx[(t / kTilesPerIdx) & 1];
+    const int jt = key0 + t * kKeysPerTile;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int kk = 8 * wave + i;
+      const int slot = idx[min(jt + kk, key1 - 1) - blk_first];
+      const uint16_t* row = p.kv_pool + (int64_t)slot * p.kv_row_stride;
+      __builtin_amdgcn_global_load_lds(row + lane * 8, MLAV_LDS(void, stage + kk * kVStride), 16, 0, 0);
+    }
+    {
+      const int kk = 8 * wave + (lane >> 3);
+      const int slot = idx[min(jt + kk, key1 - 1) - blk_first];
+      const uint16_t* row = p.kv_pool + (int64_t)slot * p.kv_row_stride;
+      const int unit = (lane & 7) ^ (kk & 7);
+      __builtin_amdgcn_global_load_lds(row + kDv + unit * 8,
+                                       MLAV_LDS(void, stage + kVPart + (8 * wave) * 128), 16, 0, 0);
+    }
+  };
+
+  f32x4 o[kDv / 16][kRowTiles];
+  float m_run[kRowTiles], l_run[kRowTiles];
+#pragma unroll
+  for (int rt = 0; rt < kRowTiles; ++rt) {
+#pragma unroll
+    for (int dt = 0; dt < kDv / 16; ++dt) o[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[rt] = -INFINITY;
+    l_run[rt] = 0.f;
+  }
+
+  // per-lane LDS offsets of the MFMA operand reads (within a stage)
+  //   K for S^T (A operand): key 16kt + n, 16-byte unit 4ks + g
+  const int k_off = n * kVStride + g * 16;
+  const int r_off = kVPart + n * 128 + ((g ^ (n & 7)) * 16);          // ks = 16
+  const int r_off2 = kVPart + n * 128 + (((4 + g) ^ (n & 7)) * 16);   // ks = 17
+  //   V^T for PV (A operand, transposed read): lane s = 4k + j of group g
+  //   points at key 4g + k, dims 16dt + 4j
+  const int v_off = (4 * g + (n >> 2)) * kVStride + (n & 3) * 8;
+
+  load_idx(0);
+  store_idx(0);
+  if (ntiles > kTilesPerIdx) load_idx(1);
+  wait_vm_barrier(0);
+  for (int t = 0; t < kStages - 1 && t < ntiles; ++t) issue(t);
+
+  for (int t = 0; t < ntiles; ++t) {
+    wait_vm_barrier(9 * min(kStages - 2, ntiles - 1 - t));
+    if (t + kStages - 1 < ntiles) issue(t + kStages - 1);
+    if ((t + kStages) % kTilesPerIdx == 0 && t + kStages < ntiles) {
+      const int blk = (t + kStages) / kTilesPerIdx;
+      store_idx(blk);
+      if ((blk + 1) * kTilesPerIdx < ntiles) load_idx(blk + 1);
+    }
+    if (!wave_active) continue;
+
+    const unsigned char* stage = s_tiles + (t % kStages) * kStageBytes;
+    const int jt = key0 + t * kKeysPerTile;
+    // S^T = K . Q^T: 32 keys x kRowsPerWave rows, K-dim 576.  Operand reads run one step
+    // ahead of the MFMAs; the scheduling barriers keep it that way (hoisting
+    // all reads of a tile would need more registers than the wave has).
+    f32x4 sacc[2][kRowTiles];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int rt = 0; rt < kRowTiles; ++rt) sacc[kt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto k_operand = [&](int kt, int ks) -> bf16x8 {
+      const unsigned char* ap = ks < 16 ? stage + 16 * kt * kVStride + k_off + ks * 64
+                                        : stage + 16 * kt * 128 + (ks == 16 ? r_off : r_off2);
+      return *reinterpret_cast<const bf16x8*>(ap);
+    };
+    bf16x8 a_next = k_operand(0, 0);
+#pragma unroll
+    for (int step = 0; step < 2 * (kDqk / 32); ++step) {
+      const int kt = step / (kDqk / 32), ks = step % (kDqk / 32);
+      const bf16x8 a = a_next;
+      if (step + 1 < 2 * (kDqk / 32))
+        a_next = k_operand((step + 1) / (kDqk / 32), (step + 1) % (kDqk / 32));
+#pragma unroll
+      for (int rt = 0; rt < kRowTiles; ++rt)
+        sacc[kt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[rt][ks], sacc[kt][rt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // scores in base-2 units; mask the range tail and invisible tree keys
+    const bool need_mask = jt + kKeysPerTile > min(P, key1);
+    float mx[kRowTiles];
+    bool need[kRowTiles];
+    bool any_need = false;
+#pragma unroll
+    for (int rt = 0; rt < kRowTiles; ++rt) {
+      mx[rt] = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int j = t0 + 16 * kt + 4 * g + i;
-          float v = s[kt][i] * p.sm_scale_log2;
-          bool vis = j < key1;
-          if (j >= P) vis = vis && ((anc >> (j - P)) & 1ull);
-          v = vis ? v : -INFINITY;
-          s[kt][i] = v;
-          mx = fmaxf(mx, v);
+          float v = sacc[kt][rt][i] * p.sm_scale_log2;
+          if (need_mask) {
+            const int j = jt + 16 * kt + 4 * g + i;
+            bool vis = j < key1;
+            if (j >= P) vis = vis && ((anc[rt] >> (j - P)) & 1ull);
+            v = vis ? v : -INFINITY;
+          }
+          sacc[kt][rt][i] = v;
+          mx[rt] = fmaxf(mx[rt], v);
         }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_use);
+      mx[rt] = fmaxf(mx[rt], __shfl_xor(mx[rt], 16));
+      mx[rt] = fmaxf(mx[rt], __shfl_xor(mx[rt], 32));
+      need[rt] = mx[rt] > m_run[rt] + kRescaleSlack;
+      any_need = any_need || need[rt];
+    }
+    // lazy rescale: move a row's reference max only when the tile max exceeds
+    // it by more than 2^kRescaleSlack (then p <= 2^8 stays safe in fp32/bf16)
+    if (__builtin_amdgcn_ballot_w64(any_need) != 0) {
+#pragma unroll
+      for (int rt = 0; rt < kRowTiles; ++rt) {
+        const float m_new = need[rt] ? mx[rt] : m_run[rt];
+        const float alpha = m_new == m_run[rt] ? 1.f : __builtin_amdgcn_exp2f(m_run[rt] - m_new);
+        l_run[rt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < kDv / 16; ++dt) o[dt][rt] *= alpha;
+        m_run[rt] = m_new;
+      }
+    }
+    bf16x8 phi[kRowTiles], plo[kRowTiles];
+#pragma unroll
+    for (int rt = 0; rt < kRowTiles; ++rt) {
+      const float m_use = m_run[rt] == -INFINITY ? 0.f : m_run[rt];
       float rs = 0.f;
-      bf16x8 phi, plo;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pv = exp2f(s[kt][i] - m_use);
+          const float pv = __builtin_amdgcn_exp2f(sacc[kt][rt][i] - m_use);
           rs += pv;
           const __bf16 h = (__bf16)pv;
-          const __bf16 lo = (__bf16)(pv - (float)h);
-          phi[kt * 4 + i] = h;
-          plo[kt * 4 + i] = lo;
+          phi[rt][kt * 4 + i] = h;
+          plo[rt][kt * 4 + i] = (__bf16)(pv - (float)h);
         }
       }
       rs += __shfl_xor(rs, 16);
       rs += __shfl_xor(rs, 32);
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
+      l_run[rt] += rs;
+    }
+    // O^T += V^T . P^T, P = hi + lo; V^T read with the LDS transpose load,
+    // one 16-dim step ahead of the MFMAs
+    auto v_operand = [&](int dt) -> bf16x8 {
+      const unsigned char* vb = stage + v_off + dt * 32;
+      const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MLAV_LDS(i16x4, vb));
+      const i16x4 vc = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MLAV_LDS(i16x4, vb + 16 * kVStride));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vc, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 v_next = v_operand(0);
 #pragma unroll
-      for (int dt = 0; dt < kDv / 16; ++dt) o[dt] *= alpha;
-      // O^T += V^T . P^T with P split into bf16 hi + lo
+    for (int dt = 0; dt < kDv / 16; ++dt) {
+      const bf16x8 a = v_next;
+      if (dt + 1 < kDv / 16) v_next = v_operand(dt + 1);
 #pragma unroll
-      for (int dt = 0; dt < kDv / 16; ++dt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(s_vt + (16 * dt + n) * kVtStride + g * 16);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, o[dt], 0, 0, 0);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, o[dt], 0, 0, 0);
+      for (int rt = 0; rt < kRowTiles; ++rt) {
+        o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi[rt], o[dt][rt], 0, 0, 0);
+        o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo[rt], o[dt][rt], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
   poison = __syncthreads_or(poison);
   if (poison && tid == 0) atomicOr(&p.hdr->err, (uint32_t)MLA_VERIFY_DEVERR_SLOT_RANGE);
-  if (row_ok) {
+#pragma unroll
+  for (int rt = 0; rt < kRowTiles; ++rt) {
+    const int r_local = wave * kRowsPerWave + 16 * rt + n;
+    if (!row_ok[rt]) continue;
     float* po = p.part_o + ((size_t)item * kRowsPerItem + r_local) * kDv;
 #pragma unroll
-    for (int dt = 0; dt < kDv / 16; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * g) = o[dt];
+    for (int dt = 0; dt < kDv / 16; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * g) = o[dt][rt];
     if (g == 0) {
       float* pm = p.part_ml + ((size_t)item * kRowsPerItem + r_local) * 2;
-      pm[0] = m_run;
-      pm[1] = poison ? NAN : l_run;
+      pm[0] = m_run[rt];
+      pm[1] = poison ? NAN : l_run[rt];
     }
   }
 }
