@@ -110,6 +110,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-calls", type=int, default=20,
                     help="extra calls each preceded by a 1 GiB cache scrub (reported, not the value)")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="also run one device-to-device copy of this many MiB (a known-size "
+                         "kernel for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -146,6 +149,15 @@ def main():
         evs[2].record(stream)
         B.run_phase(ver.plan, a, ver.workspace, B.PHASE_MERGE, sp)
         evs[3].record(stream)
+
+    if args.calibration_copy_mib > 0:
+        n = args.calibration_copy_mib << 18          # float32 elements
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

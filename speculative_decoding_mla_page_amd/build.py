@@ -22,6 +22,10 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
     # no packed fp32 instructions in any generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in VGPRs: the split-partial kernel's O accumulator
+    # is rescaled in place, and the AGPR form makes the compiler copy it
+    # between register files on every key tile
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -15,10 +15,11 @@ constexpr int kRowTiles = 1;               // 16-row MFMA tiles of query rows pe
 constexpr int kRowsPerWave = 16 * kRowTiles;
 constexpr int kRowsPerItem = kWaves * kRowsPerWave;  // query rows per work item
 constexpr int kStages = 4;                 // key tiles in flight through LDS
-constexpr int kIdxKeys = 1024;             // slots staged per index block (32 tiles)
+constexpr int kIdxKeys = 512;              // slots staged per index block (16 tiles)
 constexpr int kPartialThreads = kWaves * 64;
 constexpr int kMetaThreads = 256;
-constexpr int kMergeThreads = 128;         // 128 lanes x 4 dims = 512
+constexpr int kMergeThreads = 256;         // 4 waves per output row, each lane 8 of the 512 dims
+constexpr int kMinChunkKeys = 128;         // shortest key range of a work item
 constexpr int kMaxBatch = 1024;            // per-request tables live in LDS of the metadata kernel
 constexpr uint32_t kPlanMagic = 0x5641'4c4du;  // "MLAV"
 

@@ -33,14 +33,19 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // LDS layout of one staged tile of kKeysPerTile keys (one pipeline stage):
-//   V part   : key k's dims [0, 512) at k * kVStride; the 16 spare bytes per row
-//              put the 16 keys an MFMA operand read touches in distinct banks.
+//   V part   : key k's dims [0, 512) at k * 1024, its 64 16-byte units stored
+//              at unit ^ vswz(k);
 //   rope part: key k's dims [512, 576) at kVPart + k * 128, its eight 16-byte
-//              units stored at unit ^ (k & 7) (the rows of eight keys are
-//              written by one 1 KB direct-to-LDS load, so they cannot be padded).
-constexpr int kVStride = kDv * 2 + 16;                   // 1040 bytes
-constexpr int kVPart = kKeysPerTile * kVStride;          // 33280
-constexpr int kStageBytes = kVPart + kKeysPerTile * 128; // 37376
+//              units stored at unit ^ rswz(k).
+// Every row is written by one 1 KB direct-to-LDS load (one V row, or the rope
+// rows of eight keys), so rows cannot be padded; the swizzles instead spread
+// the MFMA operand reads over the banks: the 16 keys of a K-operand read land
+// on 16 distinct 16-byte bank groups.
+constexpr int kVStride = kDv * 2;                        // 1024 bytes
+constexpr int kVPart = kKeysPerTile * kVStride;          // 32768
+constexpr int kStageBytes = kVPart + kKeysPerTile * 128; // 36864
+__device__ __forceinline__ int vswz(int k) { return k & 15; }
+__device__ __forceinline__ int rswz(int k) { return (k >> 1) & 7; }
 constexpr int kTilesPerIdx = kIdxKeys / kKeysPerTile;    // 32
 constexpr float kRescaleSlack = 8.f;  // rescale O only when a row max grows by > 2^8
 
@@ -113,7 +118,7 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
   if (tid == 0) {
     const long long per = (s_work + p.target_items - 1) / p.target_items;
     long long chunk = ((per + kKeysPerTile - 1) / kKeysPerTile) * kKeysPerTile;
-    if (chunk < kKeysPerTile) chunk = kKeysPerTile;
+    if (chunk < kMinChunkKeys) chunk = kMinChunkKeys;
     if (chunk > (1LL << 30)) chunk = 1LL << 30;
     s_chunk = (int)chunk;
     int items = 0;
@@ -192,7 +197,13 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// split partial: one workgroup (4 waves x kRowsPerWave query rows) per work item
+// split partial: one workgroup of 4 waves per work item (64 query rows x one
+// key range).
+//   S and softmax: wave w owns query rows 16w..16w+15 (one 16-row MFMA tile):
+//     S^T = K . Q^T over the 32 keys of a tile, online softmax, P = hi + lo.
+//   PV: wave w owns dims [128w, 128w + 128) of O for all 64 rows; P of every
+//     row tile (and its rescale factors) is exchanged through LDS, so each
+//     wave reads only its quarter of V with the LDS transpose load.
 // ---------------------------------------------------------------------------
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define MLAV_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
@@ -207,10 +218,39 @@ __device__ __forceinline__ void wait_vm_barrier(int n) {
   else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 static_assert(kStages == 4, "wait_vm_barrier covers up to two tiles (18 loads) in flight");
+// Barrier for LDS data only (the tile loads in flight keep going).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Row reductions over the four lane groups that hold one query row (lanes
+// n, n+16, n+32, n+48): the gfx950 swaps exchange 16-lane rows (xor 16) and
+// 32-lane halves (xor 32) in the VALU, with no LDS round trip.
+__device__ __forceinline__ float group_max(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group_sum(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+constexpr int kKRing = 6;                  // K operand reads in flight ahead of the S MFMAs
+constexpr int kVRing = 3;                  // V operand reads in flight ahead of the PV MFMAs
+constexpr int kDvPerWave = kDv / kWaves;   // 128 dims of O per wave
+constexpr int kDtPerWave = kDvPerWave / 16;
+static_assert(kRowTiles == 1 && kWaves == 4, "one 16-row tile per wave, four waves");
 
 __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char s_tiles[kStages * kStageBytes];
   __shared__ int32_t s_idx[2][kIdxKeys];
+  __shared__ bf16x8 s_p[kWaves][2][64];      // P of row tile w: hi, lo, in B-operand lane order
+  __shared__ float s_alpha[kRowsPerItem];    // rescale factor of each row (valid when flagged)
+  __shared__ uint32_t s_rescale[kWaves];     // row tile w rescaled this tile
 
   // Work items of one key range sit on one XCD: workgroup b is dispatched to
   // XCD b % 8, so XCD x gets the contiguous items [x*per, (x+1)*per) and the
@@ -229,33 +269,31 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
   const int P = rq[RQ_P], q0 = rq[RQ_Q0], kv0 = rq[RQ_KV0];
   const int H = p.num_heads;
   const int ntiles = (key1 - key0 + kKeysPerTile - 1) / kKeysPerTile;
+  const int nrt = (nrows + 15) >> 4;         // row tiles with at least one row
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
 
-  // query rows of this lane, one per 16-row tile rt; rows are (node, head)
+  // this wave's query row tile: row 16w + n of the item; rows are (node, head)
   // pairs with heads fastest
-  bf16x8 qf[kRowTiles][kDqk / 32];
-  uint64_t anc[kRowTiles];
-  bool row_ok[kRowTiles];
-#pragma unroll
-  for (int rt = 0; rt < kRowTiles; ++rt) {
-    const int r_local = wave * kRowsPerWave + 16 * rt + n;
-    row_ok[rt] = r_local < nrows;
+  const int r_local = 16 * wave + n;
+  const bool row_ok = r_local < nrows;
+  const bool s_active = wave < nrt;
+  bf16x8 qf[kDqk / 32];
+  uint64_t anc;
+  {
     const int r = row0 + r_local;
     const int tok = q0 + r / H, head = r % H;
     const uint16_t* qrow = p.q + (int64_t)tok * p.q_stride_tok + (int64_t)head * p.q_stride_head;
 #pragma unroll
     for (int ks = 0; ks < kDqk / 32; ++ks) {
-      u32x4 v = row_ok[rt] ? *reinterpret_cast<const u32x4*>(qrow + ks * 32 + g * 8)
-                           : u32x4{0u, 0u, 0u, 0u};
-      qf[rt][ks] = __builtin_bit_cast(bf16x8, v);
+      u32x4 v = row_ok ? *reinterpret_cast<const u32x4*>(qrow + ks * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
+      qf[ks] = __builtin_bit_cast(bf16x8, v);
     }
-    anc[rt] = row_ok[rt] ? p.anc[tok] : 0ull;
+    anc = row_ok ? p.anc[tok] : 0ull;
   }
-  const bool wave_active = wave * kRowsPerWave < nrows;
   const bool trace = (p.flags & MLA_VERIFY_FLAG_TRACE_KEYS) && rb == 0;
   const int64_t trace0 = (int64_t)kv0 + q0;
 
@@ -316,38 +354,59 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int kk = 8 * wave + i;
-      const int slot = idx[min(jt + kk, key1 - 1) - blk_first];
+      // one key per load: the slot is wave-uniform, so the row address is
+      // formed on the scalar unit
+      const int slot = __builtin_amdgcn_readfirstlane(idx[min(jt + kk, key1 - 1) - blk_first]);
       const uint16_t* row = p.kv_pool + (int64_t)slot * p.kv_row_stride;
-      __builtin_amdgcn_global_load_lds(row + lane * 8, MLAV_LDS(void, stage + kk * kVStride), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(row + (lane ^ vswz(kk)) * 8, MLAV_LDS(void, stage + kk * kVStride),
+                                       16, 0, 0);
     }
     {
       const int kk = 8 * wave + (lane >> 3);
       const int slot = idx[min(jt + kk, key1 - 1) - blk_first];
       const uint16_t* row = p.kv_pool + (int64_t)slot * p.kv_row_stride;
-      const int unit = (lane & 7) ^ (kk & 7);
+      const int unit = (lane & 7) ^ rswz(kk);
       __builtin_amdgcn_global_load_lds(row + kDv + unit * 8,
                                        MLAV_LDS(void, stage + kVPart + (8 * wave) * 128), 16, 0, 0);
     }
   };
 
-  f32x4 o[kDv / 16][kRowTiles];
-  float m_run[kRowTiles], l_run[kRowTiles];
+  // O for all 64 rows, dims [128w, 128w + 128): o[dt][rt] holds, in lane
+  // (g, n), O[row 16rt + n][dim 128w + 16dt + 4g + i]
+  f32x4 o[kDtPerWave][kWaves];
 #pragma unroll
-  for (int rt = 0; rt < kRowTiles; ++rt) {
+  for (int dt = 0; dt < kDtPerWave; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < kDv / 16; ++dt) o[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m_run[rt] = -INFINITY;
-    l_run[rt] = 0.f;
+    for (int rt = 0; rt < kWaves; ++rt) o[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;   // softmax state of this lane's row (row tile = wave)
+
+  // per-lane LDS offsets of the MFMA operand reads (within a stage).  The
+  // swizzles only touch the low 4 bits of a 16-byte unit index, so each lane
+  // keeps one offset per value of those bits and the rest of every address is
+  // an instruction immediate.
+  //   K for S^T (A operand): key 16kt + n, unit 4ks + g (ks < 16) ->
+  //   k_lo[ks & 3] + 256 (ks >> 2) + 16 kt * 1024; rope unit 4(ks - 16) + g
+  int k_lo[4];
+#pragma unroll
+  for (int kq = 0; kq < 4; ++kq) k_lo[kq] = n * kVStride + (((4 * kq + g) ^ vswz(n)) << 4);
+  const int r_off = kVPart + n * 128 + ((g ^ rswz(n)) * 16);          // ks = 16
+  const int r_off2 = kVPart + n * 128 + (((4 + g) ^ rswz(n)) * 16);   // ks = 17
+  //   V^T for PV (A operand, transposed read): lane s = 4k + j of group g
+  //   points at key 4g + k (and 16 + 4g + k), dims 128w + 16dt + 4j, i.e.
+  //   unit 16w + 2dt + (j >> 1), byte 8 (j & 1)
+  int v_lo[kDtPerWave];
+  {
+    const int v_key = 4 * g + (n >> 2);
+#pragma unroll
+    for (int dt = 0; dt < kDtPerWave; ++dt)
+      v_lo[dt] = v_key * kVStride + (n & 1) * 8 +
+                 (((16 * wave + 2 * dt + ((n >> 1) & 1)) ^ vswz(v_key)) << 4);
   }
 
-  // per-lane LDS offsets of the MFMA operand reads (within a stage)
-  //   K for S^T (A operand): key 16kt + n, 16-byte unit 4ks + g
-  const int k_off = n * kVStride + g * 16;
-  const int r_off = kVPart + n * 128 + ((g ^ (n & 7)) * 16);          // ks = 16
-  const int r_off2 = kVPart + n * 128 + (((4 + g) ^ (n & 7)) * 16);   // ks = 17
-  //   V^T for PV (A operand, transposed read): lane s = 4k + j of group g
-  //   points at key 4g + k, dims 16dt + 4j
-  const int v_off = (4 * g + (n >> 2)) * kVStride + (n & 3) * 8;
+  // row tiles without rows contribute P = 0 and never rescale
+  s_p[wave][0][lane] = bf16x8{};
+  s_p[wave][1][lane] = bf16x8{};
+  if (lane == 0) s_rescale[wave] = 0;
 
   load_idx(0);
   store_idx(0);
@@ -363,113 +422,118 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
       store_idx(blk);
       if ((blk + 1) * kTilesPerIdx < ntiles) load_idx(blk + 1);
     }
-    if (!wave_active) continue;
-
     const unsigned char* stage = s_tiles + (t % kStages) * kStageBytes;
     const int jt = key0 + t * kKeysPerTile;
-    // S^T = K . Q^T: 32 keys x kRowsPerWave rows, K-dim 576.  Operand reads run one step
-    // ahead of the MFMAs; the scheduling barriers keep it that way (hoisting
-    // all reads of a tile would need more registers than the wave has).
-    f32x4 sacc[2][kRowTiles];
+
+    if (s_active) {
+      // S^T = K . Q^T: 32 keys x 16 rows, K-dim 576.  Operand reads run
+      // kKRing steps ahead of the MFMAs; the scheduling barriers keep that
+      // order (hoisting every read of a tile would exhaust the registers).
+      constexpr int kSSteps = 2 * (kDqk / 32);
+      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      auto k_operand = [&](int step) -> bf16x8 {
+        const int kt = step / (kDqk / 32), ks = step % (kDqk / 32);
+        const unsigned char* ap = ks < 16 ? stage + k_lo[ks & 3] + (ks >> 2) * 256 + 16 * kt * kVStride
+                                          : stage + 16 * kt * 128 + (ks == 16 ? r_off : r_off2);
+        return *reinterpret_cast<const bf16x8*>(ap);
+      };
+      bf16x8 ka[kKRing];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int i = 0; i < kKRing; ++i) ka[i] = k_operand(i);
 #pragma unroll
-      for (int rt = 0; rt < kRowTiles; ++rt) sacc[kt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto k_operand = [&](int kt, int ks) -> bf16x8 {
-      const unsigned char* ap = ks < 16 ? stage + 16 * kt * kVStride + k_off + ks * 64
-                                        : stage + 16 * kt * 128 + (ks == 16 ? r_off : r_off2);
-      return *reinterpret_cast<const bf16x8*>(ap);
-    };
-    bf16x8 a_next = k_operand(0, 0);
-#pragma unroll
-    for (int step = 0; step < 2 * (kDqk / 32); ++step) {
-      const int kt = step / (kDqk / 32), ks = step % (kDqk / 32);
-      const bf16x8 a = a_next;
-      if (step + 1 < 2 * (kDqk / 32))
-        a_next = k_operand((step + 1) / (kDqk / 32), (step + 1) % (kDqk / 32));
-#pragma unroll
-      for (int rt = 0; rt < kRowTiles; ++rt)
-        sacc[kt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[rt][ks], sacc[kt][rt], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // scores in base-2 units; mask the range tail and invisible tree keys
-    const bool need_mask = jt + kKeysPerTile > min(P, key1);
-    float mx[kRowTiles];
-    bool need[kRowTiles];
-    bool any_need = false;
-#pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt) {
-      mx[rt] = -INFINITY;
+      for (int step = 0; step < kSSteps; ++step) {
+        const int kt = step / (kDqk / 32), ks = step % (kDqk / 32);
+        const bf16x8 a = ka[step % kKRing];
+        if (step + kKRing < kSSteps) ka[step % kKRing] = k_operand(step + kKRing);
+        sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], sacc[kt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      // scores in base-2 units; mask the range tail and invisible tree keys
+      const bool need_mask = jt + kKeysPerTile > min(P, key1);
+      float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float v = sacc[kt][rt][i] * p.sm_scale_log2;
+          float v = sacc[kt][i] * p.sm_scale_log2;
           if (need_mask) {
             const int j = jt + 16 * kt + 4 * g + i;
             bool vis = j < key1;
-            if (j >= P) vis = vis && ((anc[rt] >> (j - P)) & 1ull);
+            if (j >= P) vis = vis && ((anc >> (j - P)) & 1ull);
             v = vis ? v : -INFINITY;
           }
-          sacc[kt][rt][i] = v;
-          mx[rt] = fmaxf(mx[rt], v);
+          sacc[kt][i] = v;
+          mx = fmaxf(mx, v);
         }
       }
-      mx[rt] = fmaxf(mx[rt], __shfl_xor(mx[rt], 16));
-      mx[rt] = fmaxf(mx[rt], __shfl_xor(mx[rt], 32));
-      need[rt] = mx[rt] > m_run[rt] + kRescaleSlack;
-      any_need = any_need || need[rt];
-    }
-    // lazy rescale: move a row's reference max only when the tile max exceeds
-    // it by more than 2^kRescaleSlack (then p <= 2^8 stays safe in fp32/bf16)
-    if (__builtin_amdgcn_ballot_w64(any_need) != 0) {
-#pragma unroll
-      for (int rt = 0; rt < kRowTiles; ++rt) {
-        const float m_new = need[rt] ? mx[rt] : m_run[rt];
-        const float alpha = m_new == m_run[rt] ? 1.f : __builtin_amdgcn_exp2f(m_run[rt] - m_new);
-        l_run[rt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < kDv / 16; ++dt) o[dt][rt] *= alpha;
-        m_run[rt] = m_new;
+      mx = group_max(mx);
+      // lazy rescale: move a row's reference max only when the tile max
+      // exceeds it by more than 2^kRescaleSlack (then p <= 2^8 stays safe)
+      const bool need = mx > m_run + kRescaleSlack;
+      const bool any_need = __builtin_amdgcn_ballot_w64(need) != 0;
+      if (any_need) {
+        const float m_new = need ? mx : m_run;
+        const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+        m_run = m_new;
+        if (g == 0) s_alpha[r_local] = alpha;
       }
-    }
-    bf16x8 phi[kRowTiles], plo[kRowTiles];
-#pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt) {
-      const float m_use = m_run[rt] == -INFINITY ? 0.f : m_run[rt];
+      if (lane == 0) s_rescale[wave] = any_need;
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
       float rs = 0.f;
+      bf16x8 phi, plo;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(sacc[kt][rt][i] - m_use);
+          const float pv = __builtin_amdgcn_exp2f(sacc[kt][i] - m_use);
           rs += pv;
           const __bf16 h = (__bf16)pv;
-          phi[rt][kt * 4 + i] = h;
-          plo[rt][kt * 4 + i] = (__bf16)(pv - (float)h);
+          phi[kt * 4 + i] = h;
+          plo[kt * 4 + i] = (__bf16)(pv - (float)h);
         }
       }
-      rs += __shfl_xor(rs, 16);
-      rs += __shfl_xor(rs, 32);
-      l_run[rt] += rs;
+      l_run += group_sum(rs);
+      s_p[wave][0][lane] = phi;
+      s_p[wave][1][lane] = plo;
     }
-    // O^T += V^T . P^T, P = hi + lo; V^T read with the LDS transpose load,
-    // one 16-dim step ahead of the MFMAs
+    lds_barrier();
+
+    // PV on this wave's 128 dims for every row tile: O^T += V^T . P^T.  Row
+    // tiles without rows carry P = 0, so the loop below has no branches (a
+    // branch would make the compiler settle every outstanding LDS read).
+    bf16x8 ph[kWaves], pl[kWaves];
+#pragma unroll
+    for (int rt = 0; rt < kWaves; ++rt) {
+      ph[rt] = s_p[rt][0][lane];
+      pl[rt] = s_p[rt][1][lane];
+    }
+    if ((s_rescale[0] | s_rescale[1] | s_rescale[2] | s_rescale[3]) != 0) {
+#pragma unroll
+      for (int rt = 0; rt < kWaves; ++rt) {
+        const float alpha = s_rescale[rt] ? s_alpha[16 * rt + n] : 1.f;
+#pragma unroll
+        for (int dt = 0; dt < kDtPerWave; ++dt) o[dt][rt] *= alpha;
+      }
+    }
     auto v_operand = [&](int dt) -> bf16x8 {
-      const unsigned char* vb = stage + v_off + dt * 32;
+      const unsigned char* vb = stage + v_lo[dt];
       const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MLAV_LDS(i16x4, vb));
       const i16x4 vc = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MLAV_LDS(i16x4, vb + 16 * kVStride));
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vc, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    bf16x8 v_next = v_operand(0);
+    bf16x8 va_ring[kVRing];
 #pragma unroll
-    for (int dt = 0; dt < kDv / 16; ++dt) {
-      const bf16x8 a = v_next;
-      if (dt + 1 < kDv / 16) v_next = v_operand(dt + 1);
+    for (int i = 0; i < kVRing; ++i) va_ring[i] = v_operand(i);
 #pragma unroll
-      for (int rt = 0; rt < kRowTiles; ++rt) {
-        o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi[rt], o[dt][rt], 0, 0, 0);
-        o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo[rt], o[dt][rt], 0, 0, 0);
+    for (int dt = 0; dt < kDtPerWave; ++dt) {
+      const bf16x8 a = va_ring[dt % kVRing];
+      if (dt + kVRing < kDtPerWave) va_ring[dt % kVRing] = v_operand(dt + kVRing);
+#pragma unroll
+      for (int rt = 0; rt < kWaves; ++rt) {
+        o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph[rt], o[dt][rt], 0, 0, 0);
+        o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[rt], o[dt][rt], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -478,86 +542,127 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
   poison = __syncthreads_or(poison);
   if (poison && tid == 0) atomicOr(&p.hdr->err, (uint32_t)MLA_VERIFY_DEVERR_SLOT_RANGE);
 #pragma unroll
-  for (int rt = 0; rt < kRowTiles; ++rt) {
-    const int r_local = wave * kRowsPerWave + 16 * rt + n;
-    if (!row_ok[rt]) continue;
-    float* po = p.part_o + ((size_t)item * kRowsPerItem + r_local) * kDv;
+  for (int rt = 0; rt < kWaves; ++rt) {
+    const int rl = 16 * rt + n;
+    if (rl >= nrows) continue;
+    float* po = p.part_o + ((size_t)item * kRowsPerItem + rl) * kDv + kDvPerWave * wave;
 #pragma unroll
-    for (int dt = 0; dt < kDv / 16; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * g) = o[dt][rt];
-    if (g == 0) {
-      float* pm = p.part_ml + ((size_t)item * kRowsPerItem + r_local) * 2;
-      pm[0] = m_run[rt];
-      pm[1] = poison ? NAN : l_run[rt];
-    }
+    for (int dt = 0; dt < kDtPerWave; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * g) = o[dt][rt];
+  }
+  if (row_ok && g == 0) {
+    float* pm = p.part_ml + ((size_t)item * kRowsPerItem + r_local) * 2;
+    pm[0] = m_run;
+    pm[1] = poison ? NAN : l_run;
   }
 }
 
 // ---------------------------------------------------------------------------
-// merge: one workgroup of 128 lanes per query row (token, head)
+// merge: one workgroup per query row (token, head).  Wave w combines the
+// row's partials c = w, w + 4, ... (lane = 8 of the 512 dims); the four wave
+// sums are then added in LDS.  Each partial carries (O, m, l) relative to its
+// own reference max m (base-2 units); with m* = max_c m_c the row is
+// sum_c 2^(m_c - m*) O_c / sum_c 2^(m_c - m*) l_c.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(KernelParams p) {
-  __shared__ float s_red[kMergeThreads / 64];
+  constexpr int kMW = kMergeThreads / 64;
+  __shared__ float s_red[kMW];
+  __shared__ f32x4 s_acc[kMW - 1][2][64];
+  __shared__ float s_l[kMW - 1];
   const int H = p.num_heads;
   const int row = blockIdx.x;
   const int t = row / H, h = row % H;
   const WsHeader* hdr = p.hdr;
   if (t >= hdr->total_q) return;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float* outp = p.out + (int64_t)t * p.out_stride_tok + (int64_t)h * p.out_stride_head;
   float* lsep = p.lse ? p.lse + (int64_t)t * p.lse_stride_tok + h : nullptr;
   if (hdr->err & kMetaErrMask) {
-    *reinterpret_cast<f32x4*>(outp + 4 * tid) = f32x4{NAN, NAN, NAN, NAN};
+    if (tid < 128) *reinterpret_cast<f32x4*>(outp + 4 * tid) = f32x4{NAN, NAN, NAN, NAN};
     if (lsep && tid == 0) *lsep = NAN;
     return;
   }
-  // request of token t
+  // request of token t: the last request starting at or before t holds it
   const int B = hdr->batch;
   int lo = 0, hi = B - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (p.req[mid * 8 + RQ_Q0] <= t) lo = mid; else hi = mid - 1;
   }
-  const int b = lo;  // last request starting at or before t: it holds t
-  const int32_t* rq = p.req + b * 8;
+  const int32_t* rq = p.req + lo * 8;
   const int r = (t - rq[RQ_Q0]) * H + h;
   const int rb = r / kRowsPerItem, lr = r % kRowsPerItem;
   const int chunks = rq[RQ_CHUNKS], rbs = rq[RQ_RB], base = rq[RQ_ITEM0];
+  auto item_of = [&](int c) { return (size_t)(base + c * rbs + rb) * kRowsPerItem + lr; };
 
   float mloc = -INFINITY;
-  for (int c = tid; c < chunks; c += kMergeThreads) {
-    const int it = base + c * rbs + rb;
-    mloc = fmaxf(mloc, p.part_ml[((size_t)it * kRowsPerItem + lr) * 2]);
-  }
+  for (int c = tid; c < chunks; c += kMergeThreads) mloc = fmaxf(mloc, p.part_ml[item_of(c) * 2]);
   for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
-  if ((tid & 63) == 0) s_red[tid >> 6] = mloc;
+  if (lane == 0) s_red[wave] = mloc;
   __syncthreads();
   float mstar = s_red[0];
-  for (int w = 1; w < kMergeThreads / 64; ++w) mstar = fmaxf(mstar, s_red[w]);
+#pragma unroll
+  for (int w = 1; w < kMW; ++w) mstar = fmaxf(mstar, s_red[w]);
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   if (mstar != -INFINITY) {
-    for (int c = 0; c < chunks; ++c) {
-      const int it = base + c * rbs + rb;
-      const float* pm = p.part_ml + ((size_t)it * kRowsPerItem + lr) * 2;
-      const float w = exp2f(pm[0] - mstar);
-      L += w * pm[1];
-      const f32x4 v = *reinterpret_cast<const f32x4*>(p.part_o + ((size_t)it * kRowsPerItem + lr) * kDv + 4 * tid);
-      acc += w * v;
+    int c = wave;
+    for (; c + 3 * kMW < chunks; c += 4 * kMW) {
+      f32x4 v[4][2];
+      float m[4], l[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const size_t ix = item_of(c + u * kMW);
+        m[u] = p.part_ml[ix * 2];
+        l[u] = p.part_ml[ix * 2 + 1];
+        const float* po = p.part_o + ix * kDv + 8 * lane;
+        v[u][0] = *reinterpret_cast<const f32x4*>(po);
+        v[u][1] = *reinterpret_cast<const f32x4*>(po + 4);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = __builtin_amdgcn_exp2f(m[u] - mstar);
+        L += w * l[u];
+        acc0 += w * v[u][0];
+        acc1 += w * v[u][1];
+      }
+    }
+    for (; c < chunks; c += kMW) {
+      const size_t ix = item_of(c);
+      const float w = __builtin_amdgcn_exp2f(p.part_ml[ix * 2] - mstar);
+      L += w * p.part_ml[ix * 2 + 1];
+      const float* po = p.part_o + ix * kDv + 8 * lane;
+      acc0 += w * *reinterpret_cast<const f32x4*>(po);
+      acc1 += w * *reinterpret_cast<const f32x4*>(po + 4);
     }
   }
-  f32x4 res;
+  if (wave > 0) {
+    s_acc[wave - 1][0][lane] = acc0;
+    s_acc[wave - 1][1][lane] = acc1;
+    if (lane == 0) s_l[wave - 1] = L;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < kMW - 1; ++w) {
+    acc0 += s_acc[w][0][lane];
+    acc1 += s_acc[w][1][lane];
+    L += s_l[w];
+  }
+  f32x4 r0, r1;
   float lse;
   if (mstar == -INFINITY) {
-    res = f32x4{0.f, 0.f, 0.f, 0.f};
+    r0 = r1 = f32x4{0.f, 0.f, 0.f, 0.f};
     lse = -INFINITY;
   } else {
     const float inv = 1.f / L;
-    res = acc * inv;
-    lse = (mstar + log2f(L)) * 0.69314718055994531f;
+    r0 = acc0 * inv;
+    r1 = acc1 * inv;
+    lse = (mstar + __builtin_amdgcn_logf(L)) * 0.69314718055994531f;
   }
-  *reinterpret_cast<f32x4*>(outp + 4 * tid) = res;
-  if (lsep && tid == 0) *lsep = lse;
+  *reinterpret_cast<f32x4*>(outp + 8 * lane) = r0;
+  *reinterpret_cast<f32x4*>(outp + 8 * lane + 4) = r1;
+  if (lsep && lane == 0) *lsep = lse;
 }
 
 // ---------------------------------------------------------------------------
