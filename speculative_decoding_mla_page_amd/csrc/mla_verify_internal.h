@@ -14,9 +14,9 @@ constexpr int kWaves = 4;                  // waves per workgroup (one per SIMD)
 constexpr int kRowTiles = 1;               // 16-row MFMA tiles of query rows per wave
 constexpr int kRowsPerWave = 16 * kRowTiles;
 constexpr int kRowsPerItem = kWaves * kRowsPerWave;  // query rows per work item
-constexpr int kStages = 4;                 // key tiles in flight through LDS
-constexpr int kIdxKeys = 512;              // slots staged per index block (16 tiles)
-constexpr int kPartialThreads = kWaves * 64;
+constexpr int kStages = 4;                 // LDS slots of key tiles (V part)
+constexpr int kIdxKeys = 256;              // slots staged per index block (8 tiles)
+constexpr int kPartialThreads = 2 * kWaves * 64;   // score waves + PV waves
 constexpr int kMetaThreads = 256;
 constexpr int kMergeThreads = 256;         // 4 waves per output row, each lane 8 of the 512 dims
 constexpr int kMinChunkKeys = 128;         // shortest key range of a work item

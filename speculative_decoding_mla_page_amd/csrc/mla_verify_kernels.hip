@@ -32,18 +32,19 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// LDS layout of one staged tile of kKeysPerTile keys (one pipeline stage):
-//   V part   : key k's dims [0, 512) at k * 1024, its 64 16-byte units stored
-//              at unit ^ vswz(k);
-//   rope part: key k's dims [512, 576) at kVPart + k * 128, its eight 16-byte
-//              units stored at unit ^ rswz(k).
+// LDS layout of a staged tile of kKeysPerTile keys:
+//   V part   : key k's dims [0, 512) at k * 1024 in one of kStages V slots,
+//              its 64 16-byte units stored at unit ^ vswz(k);
+//   rope part: key k's dims [512, 576) at k * 128 in one of kRopeSlots rope
+//              slots (only the score waves read them), units at unit ^ rswz(k).
 // Every row is written by one 1 KB direct-to-LDS load (one V row, or the rope
 // rows of eight keys), so rows cannot be padded; the swizzles instead spread
 // the MFMA operand reads over the banks: the 16 keys of a K-operand read land
 // on 16 distinct 16-byte bank groups.
 constexpr int kVStride = kDv * 2;                        // 1024 bytes
-constexpr int kVPart = kKeysPerTile * kVStride;          // 32768
-constexpr int kStageBytes = kVPart + kKeysPerTile * 128; // 36864
+constexpr int kVSlotBytes = kKeysPerTile * kVStride;     // 32768
+constexpr int kRopeSlotBytes = kKeysPerTile * 128;       // 4096
+constexpr int kRopeSlots = 3;
 __device__ __forceinline__ int vswz(int k) { return k & 15; }
 __device__ __forceinline__ int rswz(int k) { return (k >> 1) & 7; }
 constexpr int kTilesPerIdx = kIdxKeys / kKeysPerTile;    // 32
@@ -197,13 +198,16 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// split partial: one workgroup of 4 waves per work item (64 query rows x one
-// key range).
-//   S and softmax: wave w owns query rows 16w..16w+15 (one 16-row MFMA tile):
-//     S^T = K . Q^T over the 32 keys of a tile, online softmax, P = hi + lo.
-//   PV: wave w owns dims [128w, 128w + 128) of O for all 64 rows; P of every
-//     row tile (and its rescale factors) is exchanged through LDS, so each
-//     wave reads only its quarter of V with the LDS transpose load.
+// split partial: one workgroup of 8 waves per work item (64 query rows x one
+// key range), specialised in two roles that run side by side on each SIMD:
+//   score waves 0-3: wave r owns query rows 16r..16r+15 (one 16-row MFMA
+//     tile); for tile i it forms S^T = K . Q^T, keeps the online softmax of
+//     its rows and publishes P(i) = hi + lo and the rows' rescale factors.
+//   PV waves 4-7: wave 4+r owns dims [128r, 128r+128) of O for all 64 rows;
+//     during tile i it accumulates O^T += V^T . P^T for tile i-1, reading
+//     V^T from the key-major tile with the LDS transpose load.
+// One barrier per tile hands P(i) (double buffered) from the score waves to
+// the PV waves, so the score waves' softmax overlaps the PV waves' MFMAs.
 // ---------------------------------------------------------------------------
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define MLAV_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
@@ -213,14 +217,9 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 // this wave's LDS operations, then meet the other waves.  The memory clobber
 // keeps the compiler from moving LDS accesses across the barrier.
 __device__ __forceinline__ void wait_vm_barrier(int n) {
-  if (n >= 18) asm volatile("s_waitcnt vmcnt(18) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if (n >= 9) asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (n >= 5) asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if (n >= 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-static_assert(kStages == 4, "wait_vm_barrier covers up to two tiles (18 loads) in flight");
-// Barrier for LDS data only (the tile loads in flight keep going).
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Row reductions over the four lane groups that hold one query row (lanes
@@ -241,16 +240,18 @@ __device__ __forceinline__ float group_sum(float v) {
 
 constexpr int kKRing = 6;                  // K operand reads in flight ahead of the S MFMAs
 constexpr int kVRing = 3;                  // V operand reads in flight ahead of the PV MFMAs
-constexpr int kDvPerWave = kDv / kWaves;   // 128 dims of O per wave
+constexpr int kDvPerWave = kDv / kWaves;   // 128 dims of O per PV wave
 constexpr int kDtPerWave = kDvPerWave / 16;
-static_assert(kRowTiles == 1 && kWaves == 4, "one 16-row tile per wave, four waves");
+static_assert(kRowTiles == 1 && kWaves == 4, "four score waves of 16 rows, four PV waves");
+static_assert(kTilesPerIdx >= 4, "an index block outlasts the tile prefetch");
 
 __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char s_tiles[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char s_v[kStages * kVSlotBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char s_r[kRopeSlots * kRopeSlotBytes];
+  __shared__ bf16x8 s_p[2][kWaves][2][64];      // P(i): buffer i % 2, row tile, hi/lo, lane
   __shared__ int32_t s_idx[2][kIdxKeys];
-  __shared__ bf16x8 s_p[kWaves][2][64];      // P of row tile w: hi, lo, in B-operand lane order
-  __shared__ float s_alpha[kRowsPerItem];    // rescale factor of each row (valid when flagged)
-  __shared__ uint32_t s_rescale[kWaves];     // row tile w rescaled this tile
+  __shared__ float s_alpha[2][kRowsPerItem];    // rescale factor of each row (valid when flagged)
+  __shared__ uint32_t s_rescale[2][kWaves];     // row tile rescaled at tile i
 
   // Work items of one key range sit on one XCD: workgroup b is dispatched to
   // XCD b % 8, so XCD x gets the contiguous items [x*per, (x+1)*per) and the
@@ -269,177 +270,165 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
   const int P = rq[RQ_P], q0 = rq[RQ_Q0], kv0 = rq[RQ_KV0];
   const int H = p.num_heads;
   const int ntiles = (key1 - key0 + kKeysPerTile - 1) / kKeysPerTile;
-  const int nrt = (nrows + 15) >> 4;         // row tiles with at least one row
+  const int nrt = (nrows + 15) >> 4;            // row tiles with at least one row
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool score_wave = wave < kWaves;
+  const int r = wave & (kWaves - 1);            // row tile (score) or dim quarter (PV)
   const int n = lane & 15, g = lane >> 4;
 
-  // this wave's query row tile: row 16w + n of the item; rows are (node, head)
-  // pairs with heads fastest
-  const int r_local = 16 * wave + n;
-  const bool row_ok = r_local < nrows;
-  const bool s_active = wave < nrt;
-  bf16x8 qf[kDqk / 32];
-  uint64_t anc;
-  {
-    const int r = row0 + r_local;
-    const int tok = q0 + r / H, head = r % H;
-    const uint16_t* qrow = p.q + (int64_t)tok * p.q_stride_tok + (int64_t)head * p.q_stride_head;
-#pragma unroll
-    for (int ks = 0; ks < kDqk / 32; ++ks) {
-      u32x4 v = row_ok ? *reinterpret_cast<const u32x4*>(qrow + ks * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
-      qf[ks] = __builtin_bit_cast(bf16x8, v);
-    }
-    anc = row_ok ? p.anc[tok] : 0ull;
-  }
+  const int r_local = 16 * r + n;
   const bool trace = (p.flags & MLA_VERIFY_FLAG_TRACE_KEYS) && rb == 0;
   const int64_t trace0 = (int64_t)kv0 + q0;
 
   // ---- slots: blocks of kIdxKeys keys staged in LDS (double buffered) ----
-  // load_idx only issues the index loads; store_idx (a block later) checks
-  // the slots, records the trace and writes them to LDS, so the loads never
-  // hold up the tile pipeline.
+  // threads 0..kIdxKeys-1 (the score waves) hold one key each.  load_idx only
+  // issues the index load; store_idx (a block later) checks the slot, records
+  // the trace and writes it to LDS, so the loads never hold up the tiles.
   bool poison = false;
-  uint32_t idx_lo[kIdxKeys / kPartialThreads], idx_hi[kIdxKeys / kPartialThreads];
+  uint32_t idx_lo = 0, idx_hi = 0;
   auto load_idx = [&](int blk) {
-#pragma unroll
-    for (int i = 0; i < kIdxKeys / kPartialThreads; ++i) {
-      const int j = key0 + blk * kIdxKeys + tid + kPartialThreads * i;
-      const bool prefix = j < P;
-      const void* base = prefix ? p.kv_indices : p.out_cache_loc;
-      const int64_t at = prefix ? (int64_t)kv0 + j : (int64_t)q0 + (j - P);
-      const bool wide = prefix ? p.kv_idx64 : p.ocl_idx64;
-      uint32_t lo = 0, hi = 0;
-      if (j < key1) {
-        if (wide) {
-          const uint32_t* w = reinterpret_cast<const uint32_t*>(base) + 2 * at;
-          lo = w[0];
-          hi = w[1];
-        } else {
-          lo = reinterpret_cast<const uint32_t*>(base)[at];
-        }
+    const int j = key0 + blk * kIdxKeys + tid;
+    const bool prefix = j < P;
+    const void* base = prefix ? p.kv_indices : p.out_cache_loc;
+    const int64_t at = prefix ? (int64_t)kv0 + j : (int64_t)q0 + (j - P);
+    const bool wide = prefix ? p.kv_idx64 : p.ocl_idx64;
+    uint32_t lo = 0, hi = 0;
+    if (j < key1) {
+      if (wide) {
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(base) + 2 * at;
+        lo = w[0];
+        hi = w[1];
+      } else {
+        lo = reinterpret_cast<const uint32_t*>(base)[at];
       }
-      idx_lo[i] = lo;
-      idx_hi[i] = hi;
     }
+    idx_lo = lo;
+    idx_hi = hi;
   };
   auto store_idx = [&](int blk) {
-#pragma unroll
-    for (int i = 0; i < kIdxKeys / kPartialThreads; ++i) {
-      const int j = key0 + blk * kIdxKeys + tid + kPartialThreads * i;
-      const bool wide = j < P ? p.kv_idx64 : p.ocl_idx64;
-      const int64_t slot = wide ? (int64_t)(((uint64_t)idx_hi[i] << 32) | idx_lo[i])
-                                : (int64_t)(int32_t)idx_lo[i];
-      int32_t v = 0;
-      if (j < key1) {
-        if (trace) p.trace[trace0 + j] = slot;
-        if (slot >= 0 && slot < p.num_slots) v = (int32_t)slot;
-        else poison = true;   // read slot 0 instead; the whole item's rows become NaN
-      }
-      s_idx[blk & 1][tid + kPartialThreads * i] = v;
+    const int j = key0 + blk * kIdxKeys + tid;
+    const bool wide = j < P ? p.kv_idx64 : p.ocl_idx64;
+    const int64_t slot = wide ? (int64_t)(((uint64_t)idx_hi << 32) | idx_lo) : (int64_t)(int32_t)idx_lo;
+    int32_t v = 0;
+    if (j < key1) {
+      if (trace) p.trace[trace0 + j] = slot;
+      if (slot >= 0 && slot < p.num_slots) v = (int32_t)slot;
+      else poison = true;   // read slot 0 instead; the whole item's rows become NaN
     }
+    s_idx[blk & 1][tid] = v;
   };
 
-  // ---- direct-to-LDS gather of tile t: 9 loads of 1 KB per wave ----
-  // wave w fetches keys 8w..8w+7 of the tile: one load per key for dims
-  // [0,512) (lane = 16-byte unit) and one load for the eight rope rows.  Keys
-  // past the range end re-read the range's last key (finite data, masked).
+  // ---- direct-to-LDS gather of tile t ----
+  // wave w fetches the dims [0,512) of keys 4w..4w+3 (one 1 KB load per key,
+  // lane = 16-byte unit); score wave w also fetches the rope rows of keys
+  // 8w..8w+7 (one load).  Keys past the range end re-read the range's last
+  // key (finite data, masked).  Loads per tile: 5 (score wave), 4 (PV wave).
   auto issue = [&](int t) {
-    unsigned char* stage = s_tiles + (t % kStages) * kStageBytes;
+    unsigned char* vslot = s_v + (t % kStages) * kVSlotBytes;
     const int blk_first = key0 + (t / kTilesPerIdx) * kIdxKeys;
     const int32_t* idx = s_idx[(t / kTilesPerIdx) & 1];
     const int jt = key0 + t * kKeysPerTile;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int kk = 8 * wave + i;
+    for (int i = 0; i < 4; ++i) {
+      const int kk = 4 * wave + i;
       // one key per load: the slot is wave-uniform, so the row address is
       // formed on the scalar unit
       const int slot = __builtin_amdgcn_readfirstlane(idx[min(jt + kk, key1 - 1) - blk_first]);
       const uint16_t* row = p.kv_pool + (int64_t)slot * p.kv_row_stride;
-      __builtin_amdgcn_global_load_lds(row + (lane ^ vswz(kk)) * 8, MLAV_LDS(void, stage + kk * kVStride),
+      __builtin_amdgcn_global_load_lds(row + (lane ^ vswz(kk)) * 8, MLAV_LDS(void, vslot + kk * kVStride),
                                        16, 0, 0);
     }
-    {
+    if (score_wave) {
+      unsigned char* rslot = s_r + (t % kRopeSlots) * kRopeSlotBytes;
       const int kk = 8 * wave + (lane >> 3);
       const int slot = idx[min(jt + kk, key1 - 1) - blk_first];
       const uint16_t* row = p.kv_pool + (int64_t)slot * p.kv_row_stride;
       const int unit = (lane & 7) ^ rswz(kk);
-      __builtin_amdgcn_global_load_lds(row + kDv + unit * 8,
-                                       MLAV_LDS(void, stage + kVPart + (8 * wave) * 128), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(row + kDv + unit * 8, MLAV_LDS(void, rslot + (8 * wave) * 128), 16,
+                                       0, 0);
     }
   };
+  const int loads_per_tile = score_wave ? 5 : 4;
 
-  // O for all 64 rows, dims [128w, 128w + 128): o[dt][rt] holds, in lane
-  // (g, n), O[row 16rt + n][dim 128w + 16dt + 4g + i]
-  f32x4 o[kDtPerWave][kWaves];
+  // The two roles run separate loops with the same barrier sequence: one
+  // barrier before the first tile, then one per iteration i = 0..ntiles.
+  // Iteration i: scores of tile i (score waves) || PV of tile i - 1 (PV waves).
+  // Tile i + 2 goes to V slot (i + 2) % 4, last read by PV(i - 2), and to rope
+  // slot (i + 2) % 3, last read by the scores of tile i - 1.
+  auto top_of_iteration = [&](int i) {
+    wait_vm_barrier(i + 1 < ntiles ? loads_per_tile : 0);   // tile i landed
+    if (i + 2 < ntiles) issue(i + 2);
+  };
+
+  if (score_wave) {
+    // ---- score waves: query rows 16r + n; rows are (node, head), heads fastest
+    const bool row_ok = r_local < nrows;
+    const bool s_active = r < nrt;
+    bf16x8 qf[kDqk / 32];
+    uint64_t anc;
+    {
+      const int rr = row0 + r_local;
+      const int tok = q0 + rr / H, head = rr % H;
+      const uint16_t* qrow = p.q + (int64_t)tok * p.q_stride_tok + (int64_t)head * p.q_stride_head;
 #pragma unroll
-  for (int dt = 0; dt < kDtPerWave; ++dt)
-#pragma unroll
-    for (int rt = 0; rt < kWaves; ++rt) o[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;   // softmax state of this lane's row (row tile = wave)
-
-  // per-lane LDS offsets of the MFMA operand reads (within a stage).  The
-  // swizzles only touch the low 4 bits of a 16-byte unit index, so each lane
-  // keeps one offset per value of those bits and the rest of every address is
-  // an instruction immediate.
-  //   K for S^T (A operand): key 16kt + n, unit 4ks + g (ks < 16) ->
-  //   k_lo[ks & 3] + 256 (ks >> 2) + 16 kt * 1024; rope unit 4(ks - 16) + g
-  int k_lo[4];
-#pragma unroll
-  for (int kq = 0; kq < 4; ++kq) k_lo[kq] = n * kVStride + (((4 * kq + g) ^ vswz(n)) << 4);
-  const int r_off = kVPart + n * 128 + ((g ^ rswz(n)) * 16);          // ks = 16
-  const int r_off2 = kVPart + n * 128 + (((4 + g) ^ rswz(n)) * 16);   // ks = 17
-  //   V^T for PV (A operand, transposed read): lane s = 4k + j of group g
-  //   points at key 4g + k (and 16 + 4g + k), dims 128w + 16dt + 4j, i.e.
-  //   unit 16w + 2dt + (j >> 1), byte 8 (j & 1)
-  int v_lo[kDtPerWave];
-  {
-    const int v_key = 4 * g + (n >> 2);
-#pragma unroll
-    for (int dt = 0; dt < kDtPerWave; ++dt)
-      v_lo[dt] = v_key * kVStride + (n & 1) * 8 +
-                 (((16 * wave + 2 * dt + ((n >> 1) & 1)) ^ vswz(v_key)) << 4);
-  }
-
-  // row tiles without rows contribute P = 0 and never rescale
-  s_p[wave][0][lane] = bf16x8{};
-  s_p[wave][1][lane] = bf16x8{};
-  if (lane == 0) s_rescale[wave] = 0;
-
-  load_idx(0);
-  store_idx(0);
-  if (ntiles > kTilesPerIdx) load_idx(1);
-  wait_vm_barrier(0);
-  for (int t = 0; t < kStages - 1 && t < ntiles; ++t) issue(t);
-
-  for (int t = 0; t < ntiles; ++t) {
-    wait_vm_barrier(9 * min(kStages - 2, ntiles - 1 - t));
-    if (t + kStages - 1 < ntiles) issue(t + kStages - 1);
-    if ((t + kStages) % kTilesPerIdx == 0 && t + kStages < ntiles) {
-      const int blk = (t + kStages) / kTilesPerIdx;
-      store_idx(blk);
-      if ((blk + 1) * kTilesPerIdx < ntiles) load_idx(blk + 1);
+      for (int ks = 0; ks < kDqk / 32; ++ks) {
+        u32x4 v = row_ok ? *reinterpret_cast<const u32x4*>(qrow + ks * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
+        qf[ks] = __builtin_bit_cast(bf16x8, v);
+      }
+      anc = row_ok ? p.anc[tok] : 0ull;
     }
-    const unsigned char* stage = s_tiles + (t % kStages) * kStageBytes;
-    const int jt = key0 + t * kKeysPerTile;
+    float m_run = -INFINITY, l_run = 0.f;       // softmax state of this lane's row
+    //   K for S^T (A operand): key 16kt + n, unit 4ks + g (ks < 16) ->
+    //   k_lo[ks & 3] + 256 (ks >> 2) + 16 kt * 1024; rope unit 4(ks - 16) + g.
+    //   The swizzle only touches the low 4 bits of a unit index, so the rest
+    //   of every address is an instruction immediate.
+    int k_lo[4];
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq) k_lo[kq] = n * kVStride + (((4 * kq + g) ^ vswz(n)) << 4);
+    const int r_off = n * 128 + ((g ^ rswz(n)) * 16);          // ks = 16
+    const int r_off2 = n * 128 + (((4 + g) ^ rswz(n)) * 16);   // ks = 17
 
-    if (s_active) {
-      // S^T = K . Q^T: 32 keys x 16 rows, K-dim 576.  Operand reads run
-      // kKRing steps ahead of the MFMAs; the scheduling barriers keep that
-      // order (hoisting every read of a tile would exhaust the registers).
+    // row tiles without rows contribute P = 0 and never rescale
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      s_p[b][r][0][lane] = bf16x8{};
+      s_p[b][r][1][lane] = bf16x8{};
+      if (lane == 0) s_rescale[b][r] = 0;
+    }
+    load_idx(0);
+    store_idx(0);
+    if (ntiles > kTilesPerIdx) load_idx(1);
+    wait_vm_barrier(0);
+    for (int t = 0; t < 2 && t < ntiles; ++t) issue(t);
+
+    for (int i = 0; i <= ntiles; ++i) {
+      top_of_iteration(i);
+      // index block b is first needed when tile 8b is issued (iteration 8b - 2)
+      if ((i + 3) % kTilesPerIdx == 0 && i + 3 < ntiles) {
+        const int blk = (i + 3) / kTilesPerIdx;
+        store_idx(blk);
+        if ((blk + 1) * kTilesPerIdx < ntiles) load_idx(blk + 1);
+      }
+      if (!s_active || i >= ntiles) continue;
+      const unsigned char* vslot = s_v + (i % kStages) * kVSlotBytes;
+      const unsigned char* rslot = s_r + (i % kRopeSlots) * kRopeSlotBytes;
+      const int jt = key0 + i * kKeysPerTile;
+      // S^T = K . Q^T: 32 keys x 16 rows, K-dim 576; operand reads run
+      // kKRing steps ahead of the MFMAs
       constexpr int kSSteps = 2 * (kDqk / 32);
       f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       auto k_operand = [&](int step) -> bf16x8 {
         const int kt = step / (kDqk / 32), ks = step % (kDqk / 32);
-        const unsigned char* ap = ks < 16 ? stage + k_lo[ks & 3] + (ks >> 2) * 256 + 16 * kt * kVStride
-                                          : stage + 16 * kt * 128 + (ks == 16 ? r_off : r_off2);
+        const unsigned char* ap = ks < 16 ? vslot + k_lo[ks & 3] + (ks >> 2) * 256 + 16 * kt * kVStride
+                                          : rslot + 16 * kt * 128 + (ks == 16 ? r_off : r_off2);
         return *reinterpret_cast<const bf16x8*>(ap);
       };
       bf16x8 ka[kKRing];
 #pragma unroll
-      for (int i = 0; i < kKRing; ++i) ka[i] = k_operand(i);
+      for (int s = 0; s < kKRing; ++s) ka[s] = k_operand(s);
 #pragma unroll
       for (int step = 0; step < kSSteps; ++step) {
         const int kt = step / (kDqk / 32), ks = step % (kDqk / 32);
@@ -448,22 +437,21 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
         sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], sacc[kt], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
-
       // scores in base-2 units; mask the range tail and invisible tree keys
       const bool need_mask = jt + kKeysPerTile > min(P, key1);
       float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = sacc[kt][i] * p.sm_scale_log2;
+        for (int q = 0; q < 4; ++q) {
+          float v = sacc[kt][q] * p.sm_scale_log2;
           if (need_mask) {
-            const int j = jt + 16 * kt + 4 * g + i;
+            const int j = jt + 16 * kt + 4 * g + q;
             bool vis = j < key1;
             if (j >= P) vis = vis && ((anc >> (j - P)) & 1ull);
             v = vis ? v : -INFINITY;
           }
-          sacc[kt][i] = v;
+          sacc[kt][q] = v;
           mx = fmaxf(mx, v);
         }
       }
@@ -477,82 +465,107 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
         const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
         m_run = m_new;
-        if (g == 0) s_alpha[r_local] = alpha;
+        if (g == 0) s_alpha[i & 1][r_local] = alpha;
       }
-      if (lane == 0) s_rescale[wave] = any_need;
+      if (lane == 0) s_rescale[i & 1][r] = any_need;
       const float m_use = m_run == -INFINITY ? 0.f : m_run;
       float rs = 0.f;
       bf16x8 phi, plo;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(sacc[kt][i] - m_use);
+        for (int q = 0; q < 4; ++q) {
+          const float pv = __builtin_amdgcn_exp2f(sacc[kt][q] - m_use);
           rs += pv;
           const __bf16 h = (__bf16)pv;
-          phi[kt * 4 + i] = h;
-          plo[kt * 4 + i] = (__bf16)(pv - (float)h);
+          phi[kt * 4 + q] = h;
+          plo[kt * 4 + q] = (__bf16)(pv - (float)h);
         }
       }
       l_run += group_sum(rs);
-      s_p[wave][0][lane] = phi;
-      s_p[wave][1][lane] = plo;
+      s_p[i & 1][r][0][lane] = phi;
+      s_p[i & 1][r][1][lane] = plo;
     }
-    lds_barrier();
+    poison = __syncthreads_or(poison);
+    if (poison && tid == 0) atomicOr(&p.hdr->err, (uint32_t)MLA_VERIFY_DEVERR_SLOT_RANGE);
+    if (row_ok && g == 0) {
+      float* pm = p.part_ml + ((size_t)item * kRowsPerItem + r_local) * 2;
+      pm[0] = m_run;
+      pm[1] = poison ? NAN : l_run;
+    }
+  } else {
+    // ---- PV waves: O for all 64 rows, dims [128r, 128r + 128); o[dt][rt]
+    // holds, in lane (g, n), O[row 16rt + n][dim 128r + 16dt + 4g + i]
+    f32x4 o[kDtPerWave][kWaves];
+#pragma unroll
+    for (int dt = 0; dt < kDtPerWave; ++dt)
+#pragma unroll
+      for (int rt = 0; rt < kWaves; ++rt) o[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    //   V^T (A operand, transposed read): lane s = 4k + j of group g points at
+    //   key 4g + k (and 16 + 4g + k), dims 128r + 16dt + 4j, i.e. unit
+    //   16r + 2dt + (j >> 1), byte 8 (j & 1)
+    int v_lo[kDtPerWave];
+    {
+      const int v_key = 4 * g + (n >> 2);
+#pragma unroll
+      for (int dt = 0; dt < kDtPerWave; ++dt)
+        v_lo[dt] = v_key * kVStride + (n & 1) * 8 + (((16 * r + 2 * dt + ((n >> 1) & 1)) ^ vswz(v_key)) << 4);
+    }
+    wait_vm_barrier(0);
+    for (int t = 0; t < 2 && t < ntiles; ++t) issue(t);
 
-    // PV on this wave's 128 dims for every row tile: O^T += V^T . P^T.  Row
-    // tiles without rows carry P = 0, so the loop below has no branches (a
-    // branch would make the compiler settle every outstanding LDS read).
-    bf16x8 ph[kWaves], pl[kWaves];
+    for (int i = 0; i <= ntiles; ++i) {
+      top_of_iteration(i);
+      if (i == 0) continue;
+      // PV of tile i - 1 on this wave's 128 dims for every row tile.  Row
+      // tiles without rows carry P = 0, so the loop has no branches.
+      const int tp = i - 1;
+      const unsigned char* vslot = s_v + (tp % kStages) * kVSlotBytes;
+      bf16x8 ph[kWaves], pl[kWaves];
+#pragma unroll
+      for (int rt = 0; rt < kWaves; ++rt) {
+        ph[rt] = s_p[tp & 1][rt][0][lane];
+        pl[rt] = s_p[tp & 1][rt][1][lane];
+      }
+      const uint32_t* resc = s_rescale[tp & 1];
+      if ((resc[0] | resc[1] | resc[2] | resc[3]) != 0) {
+#pragma unroll
+        for (int rt = 0; rt < kWaves; ++rt) {
+          const float alpha = resc[rt] ? s_alpha[tp & 1][16 * rt + n] : 1.f;
+#pragma unroll
+          for (int dt = 0; dt < kDtPerWave; ++dt) o[dt][rt] *= alpha;
+        }
+      }
+      auto v_operand = [&](int dt) -> bf16x8 {
+        const unsigned char* vb = vslot + v_lo[dt];
+        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MLAV_LDS(i16x4, vb));
+        const i16x4 vc = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MLAV_LDS(i16x4, vb + 16 * kVStride));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vc, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      bf16x8 va_ring[kVRing];
+#pragma unroll
+      for (int s = 0; s < kVRing; ++s) va_ring[s] = v_operand(s);
+#pragma unroll
+      for (int dt = 0; dt < kDtPerWave; ++dt) {
+        const bf16x8 a = va_ring[dt % kVRing];
+        if (dt + kVRing < kDtPerWave) va_ring[dt % kVRing] = v_operand(dt + kVRing);
+#pragma unroll
+        for (int rt = 0; rt < kWaves; ++rt) {
+          o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph[rt], o[dt][rt], 0, 0, 0);
+          o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[rt], o[dt][rt], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    poison = __syncthreads_or(poison);
 #pragma unroll
     for (int rt = 0; rt < kWaves; ++rt) {
-      ph[rt] = s_p[rt][0][lane];
-      pl[rt] = s_p[rt][1][lane];
+      const int rl = 16 * rt + n;
+      if (rl >= nrows) continue;
+      float* po = p.part_o + ((size_t)item * kRowsPerItem + rl) * kDv + kDvPerWave * r;
+#pragma unroll
+      for (int dt = 0; dt < kDtPerWave; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * g) = o[dt][rt];
     }
-    if ((s_rescale[0] | s_rescale[1] | s_rescale[2] | s_rescale[3]) != 0) {
-#pragma unroll
-      for (int rt = 0; rt < kWaves; ++rt) {
-        const float alpha = s_rescale[rt] ? s_alpha[16 * rt + n] : 1.f;
-#pragma unroll
-        for (int dt = 0; dt < kDtPerWave; ++dt) o[dt][rt] *= alpha;
-      }
-    }
-    auto v_operand = [&](int dt) -> bf16x8 {
-      const unsigned char* vb = stage + v_lo[dt];
-      const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MLAV_LDS(i16x4, vb));
-      const i16x4 vc = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MLAV_LDS(i16x4, vb + 16 * kVStride));
-      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vc, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    bf16x8 va_ring[kVRing];
-#pragma unroll
-    for (int i = 0; i < kVRing; ++i) va_ring[i] = v_operand(i);
-#pragma unroll
-    for (int dt = 0; dt < kDtPerWave; ++dt) {
-      const bf16x8 a = va_ring[dt % kVRing];
-      if (dt + kVRing < kDtPerWave) va_ring[dt % kVRing] = v_operand(dt + kVRing);
-#pragma unroll
-      for (int rt = 0; rt < kWaves; ++rt) {
-        o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph[rt], o[dt][rt], 0, 0, 0);
-        o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[rt], o[dt][rt], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-
-  poison = __syncthreads_or(poison);
-  if (poison && tid == 0) atomicOr(&p.hdr->err, (uint32_t)MLA_VERIFY_DEVERR_SLOT_RANGE);
-#pragma unroll
-  for (int rt = 0; rt < kWaves; ++rt) {
-    const int rl = 16 * rt + n;
-    if (rl >= nrows) continue;
-    float* po = p.part_o + ((size_t)item * kRowsPerItem + rl) * kDv + kDvPerWave * wave;
-#pragma unroll
-    for (int dt = 0; dt < kDtPerWave; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * g) = o[dt][rt];
-  }
-  if (row_ok && g == 0) {
-    float* pm = p.part_ml + ((size_t)item * kRowsPerItem + r_local) * 2;
-    pm[0] = m_run;
-    pm[1] = poison ? NAN : l_run;
   }
 }
 
