@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MLA_VERIFY_ABI_VERSION 1
+#define MLA_VERIFY_ABI_VERSION 2
 #define MLA_VERIFY_D_QK 576          /* latent width used by Q.K^T (512 + 64 rope) */
 #define MLA_VERIFY_D_V 512           /* V = latent dims [0, 512) */
 #define MLA_VERIFY_MAX_TREE_NODES 64 /* tree visibility is packed into one 64-bit word */
@@ -109,7 +109,8 @@ typedef struct {
  *                 q + t*q_stride_tok + h*q_stride_head, 576 contiguous values;
  *                 16-byte aligned, strides multiples of 8.
  *   kv_pool       bf16 [num_slots, kv_row_stride], kv_row_stride >= 576 and a
- *                 multiple of 8, 16-byte aligned.  page_size = 1: slot s is
+ *                 multiple of 8, 16-byte aligned; num_slots < 2^31 and
+ *                 kv_row_stride < 2^30 (MLA_VERIFY_ERR_UNSUPPORTED otherwise).  page_size = 1: slot s is
  *                 one token's 576-wide latent row.  The rows of this call's
  *                 draft tokens must already be stored at out_cache_loc.
  *   qo_indptr     int32 [B+1], qo_indptr[0] = 0: request b owns query tokens
@@ -165,12 +166,16 @@ typedef struct {
   uint64_t partial_o_offset;  /* fp32 [item_capacity][rows_per_item][512] unnormalised partial outputs */
   uint64_t partial_ml_offset; /* fp32 [item_capacity][rows_per_item][2] running max (log2 units) and sum */
   uint64_t trace_offset;      /* int64 [max_kv_tokens + max_q_tokens] gathered slots; 0 without the trace flag */
+  uint64_t slots_offset;      /* int32 [max_kv_tokens + max_q_tokens] each request's keys (prefix then tree)
+                                 at kv_indptr[b] + qo_indptr[b] + j: the pool slot, -1 outside the pool */
   int32_t item_capacity;
   int32_t rows_per_item;      /* query rows (token x head) per work item */
   int32_t keys_per_tile;      /* keys staged per inner-loop step */
   int32_t target_items;
   int32_t partial_grid;       /* workgroups of the split-partial launch */
   int32_t merge_grid;         /* workgroups of the merge launch */
+  int32_t meta_grid;          /* workgroups of the metadata launch (1 + slot-staging workgroups) */
+  int32_t reserved;
 } mla_verify_layout_t;
 
 /* Validate a config and compute the plan (host arithmetic; the only possible

@@ -90,12 +90,15 @@ class Layout(ctypes.Structure):
         ("partial_o_offset", ctypes.c_uint64),
         ("partial_ml_offset", ctypes.c_uint64),
         ("trace_offset", ctypes.c_uint64),
+        ("slots_offset", ctypes.c_uint64),
         ("item_capacity", ctypes.c_int32),
         ("rows_per_item", ctypes.c_int32),
         ("keys_per_tile", ctypes.c_int32),
         ("target_items", ctypes.c_int32),
         ("partial_grid", ctypes.c_int32),
         ("merge_grid", ctypes.c_int32),
+        ("meta_grid", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 

@@ -39,6 +39,8 @@ mla_verify_status_t check_args(const PlanImpl& pl, const mla_verify_args_t* a, c
   if (!aligned(a->kv_pool, 16) || a->kv_row_stride < kDqk || a->kv_row_stride % 8 ||
       a->num_slots <= 0)
     return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  // slots are staged as int32 and row offsets formed as 32-bit x 32-bit products
+  if (a->num_slots > INT32_MAX || a->kv_row_stride > (INT32_MAX >> 1)) return MLA_VERIFY_ERR_UNSUPPORTED;
   if (!aligned(a->out, 16) || a->out_stride_tok <= 0 || a->out_stride_head <= 0 ||
       a->out_stride_tok % 4 || a->out_stride_head % 4)
     return MLA_VERIFY_ERR_INVALID_ARGUMENT;
@@ -94,6 +96,7 @@ KernelParams make_params(const PlanImpl& pl, const mla_verify_args_t* a, void* w
   p.items = reinterpret_cast<int32_t*>(base + l.items_offset);
   p.part_o = reinterpret_cast<float*>(base + l.partial_o_offset);
   p.part_ml = reinterpret_cast<float*>(base + l.partial_ml_offset);
+  p.slots = reinterpret_cast<int32_t*>(base + l.slots_offset);
   p.trace = (c.flags & MLA_VERIFY_FLAG_TRACE_KEYS) ? reinterpret_cast<int64_t*>(base + l.trace_offset)
                                                    : nullptr;
   return p;
@@ -163,6 +166,12 @@ mla_verify_status_t mla_verify_plan(const mla_verify_config_t* cfg, mla_verify_p
   // the partial kernel maps workgroups to items XCD by XCD (8 XCDs): whole groups of 8
   l.partial_grid = (int32_t)((capacity + 7) / 8 * 8);
   l.merge_grid = (int32_t)max_rows;
+  // slot staging: one workgroup per kMetaKeysPerGroup keys of capacity, at most kMetaStageGroups
+  const int64_t stage_keys = (int64_t)c.max_kv_tokens + c.max_q_tokens;
+  int64_t stage = (stage_keys + kMetaKeysPerGroup - 1) / kMetaKeysPerGroup;
+  if (stage > kMetaStageGroups) stage = kMetaStageGroups;
+  if (stage < 1) stage = 1;
+  l.meta_grid = (int32_t)(1 + stage);
 
   uint64_t off = 0;
   l.header_offset = off;
@@ -182,6 +191,8 @@ mla_verify_status_t mla_verify_plan(const mla_verify_config_t* cfg, mla_verify_p
     l.trace_offset = off;
     off = align_up(off + ((uint64_t)c.max_kv_tokens + c.max_q_tokens) * sizeof(int64_t));
   }
+  l.slots_offset = off;
+  off = align_up(off + ((uint64_t)c.max_kv_tokens + c.max_q_tokens) * sizeof(int32_t));
   l.total_bytes = off;
 
   memset(plan, 0, sizeof(*plan));

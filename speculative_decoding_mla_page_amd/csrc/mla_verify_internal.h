@@ -14,10 +14,12 @@ constexpr int kWaves = 4;                  // waves per workgroup (one per SIMD)
 constexpr int kRowTiles = 1;               // 16-row MFMA tiles of query rows per wave
 constexpr int kRowsPerWave = 16 * kRowTiles;
 constexpr int kRowsPerItem = kWaves * kRowsPerWave;  // query rows per work item
-constexpr int kStages = 4;                 // LDS slots of key tiles (V part)
+constexpr int kStages = 3;                 // LDS slots of key tiles (V part)
 constexpr int kIdxKeys = 256;              // slots staged per index block (8 tiles)
 constexpr int kPartialThreads = 2 * kWaves * 64;   // score waves + PV waves
 constexpr int kMetaThreads = 256;
+constexpr int kMetaKeysPerGroup = 1024;    // slot-staging workgroups: one per this many keys of capacity
+constexpr int kMetaStageGroups = 256;      // ... and at most this many
 constexpr int kMergeThreads = 256;         // 4 waves per output row, each lane 8 of the 512 dims
 constexpr int kMinChunkKeys = 128;         // shortest key range of a work item
 constexpr int kMaxBatch = 1024;            // per-request tables live in LDS of the metadata kernel
@@ -89,6 +91,7 @@ struct KernelParams {
   float* part_o;
   float* part_ml;
   int64_t* trace;
+  int32_t* slots;
 };
 
 int launch_meta(const KernelParams& p, const mla_verify_layout_t& lay, void* stream);

@@ -31,6 +31,7 @@ namespace mlav {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 // LDS layout of a staged tile of kKeysPerTile keys:
 //   V part   : key k's dims [0, 512) at k * 1024 in one of kStages V slots,
@@ -47,7 +48,7 @@ constexpr int kRopeSlotBytes = kKeysPerTile * 128;       // 4096
 constexpr int kRopeSlots = 3;
 __device__ __forceinline__ int vswz(int k) { return k & 15; }
 __device__ __forceinline__ int rswz(int k) { return (k >> 1) & 7; }
-constexpr int kTilesPerIdx = kIdxKeys / kKeysPerTile;    // 32
+constexpr int kTilesPerIdx = kIdxKeys / kKeysPerTile;    // 8
 constexpr float kRescaleSlack = 8.f;  // rescale O only when a row max grows by > 2^8
 
 // Key order inside a 32-key tile for the PV product.  Lane group g (lanes
@@ -61,18 +62,51 @@ __device__ __forceinline__ int64_t load_index(const void* base, int64_t i, int i
               : static_cast<int64_t>(reinterpret_cast<const int32_t*>(base)[i]);
 }
 
-// Slot of key j (combined order: prefix then tree) of a request, or -1 past the range.
-__device__ __forceinline__ int64_t key_slot(const KernelParams& p, int j, int key1, int P, int kv0,
-                                            int q0) {
-  if (j >= key1) return -1;
-  if (j < P) return load_index(p.kv_indices, (int64_t)kv0 + j, p.kv_idx64);
-  return load_index(p.out_cache_loc, (int64_t)q0 + (j - P), p.ocl_idx64);
+// ---------------------------------------------------------------------------
+// slot staging (metadata launch, workgroups 1..): every request's keys in
+// combined order (prefix keys from kv_indices, then its tree nodes' own keys
+// from out_cache_loc), at kv_indptr[b] + qo_indptr[b] + j, as int32 pool
+// slots, -1 for a slot outside [0, num_slots).  The split-partial kernel then
+// reads one contiguous, checked int32 list per request.  A request whose
+// indptrs are out of range is skipped (workgroup 0 flags it and plans no
+// work); every read stays inside the ranges the indptrs were checked against.
+// ---------------------------------------------------------------------------
+__device__ void stage_slots(const KernelParams& p, int group, int groups) {
+  const int B = p.batch;
+  if (B <= 0) return;
+  const int qB = p.qo_indptr[B];
+  const int kB = p.kv_indptr[B];
+  if (qB < 0 || qB > p.max_q_tokens || kB < 0 || (int64_t)kB > p.max_kv_tokens) return;
+  const int total = qB + kB;
+  const int per = (total + groups - 1) / groups;
+  const int g0 = group * per, g1 = min(total, g0 + per);
+  for (int g = g0 + (int)threadIdx.x; g < g1; g += kMetaThreads) {
+    int lo = 0, hi = B - 1;   // last request whose keys start at or before g
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.kv_indptr[mid] + p.qo_indptr[mid] <= g) lo = mid; else hi = mid - 1;
+    }
+    const int q0 = p.qo_indptr[lo], q1 = p.qo_indptr[lo + 1];
+    const int k0 = p.kv_indptr[lo], k1 = p.kv_indptr[lo + 1];
+    if (q0 < 0 || q1 < q0 || q1 > p.max_q_tokens || k0 < 0 || k1 < k0 || (int64_t)k1 > p.max_kv_tokens) continue;
+    const int j = g - (k0 + q0);
+    const int P = k1 - k0;
+    if (j < 0 || j >= P + (q1 - q0)) continue;
+    const int64_t raw = j < P ? load_index(p.kv_indices, (int64_t)k0 + j, p.kv_idx64)
+                              : load_index(p.out_cache_loc, (int64_t)q0 + (j - P), p.ocl_idx64);
+    p.slots[g] = (raw >= 0 && raw < p.num_slots) ? (int32_t)raw : -1;
+    if (p.trace) p.trace[g] = raw;
+  }
 }
 
 // ---------------------------------------------------------------------------
-// metadata build: one workgroup
+// metadata build: workgroup 0 (the slot staging runs beside it)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
+  if (blockIdx.x > 0) {
+    stage_slots(p, blockIdx.x - 1, gridDim.x - 1);
+    return;
+  }
   __shared__ int32_t s_req[kMaxBatch][8];
   __shared__ uint32_t s_err;
   __shared__ long long s_work;
@@ -204,10 +238,12 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
 //     tile); for tile i it forms S^T = K . Q^T, keeps the online softmax of
 //     its rows and publishes P(i) = hi + lo and the rows' rescale factors.
 //   PV waves 4-7: wave 4+r owns dims [128r, 128r+128) of O for all 64 rows;
-//     during tile i it accumulates O^T += V^T . P^T for tile i-1, reading
-//     V^T from the key-major tile with the LDS transpose load.
-// One barrier per tile hands P(i) (double buffered) from the score waves to
-// the PV waves, so the score waves' softmax overlaps the PV waves' MFMAs.
+//     during tile i it accumulates O^T += V^T . P^T for tile i-1 and moves
+//     its quarter of V^T(i) from LDS (transpose load) into registers.
+// Each iteration has two barriers: A (tile i has landed; P(i-1) is ready)
+// and B (the PV waves hold P(i-1) in registers, so the score waves may
+// overwrite it with P(i)).  Tile i's LDS slot is free once A(i+1) passes,
+// so three tiles stay in flight.
 // ---------------------------------------------------------------------------
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define MLAV_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
@@ -215,11 +251,33 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 // Wait until at most `n` vector-memory operations of this wave are still in
 // flight (direct-to-LDS loads complete in issue order and count here), finish
 // this wave's LDS operations, then meet the other waves.  The memory clobber
-// keeps the compiler from moving LDS accesses across the barrier.
+// keeps the compiler from moving LDS accesses across the barrier.  n is one
+// of 0, 4, 5 (one tile of 4 or 5 loads).
 __device__ __forceinline__ void wait_vm_barrier(int n) {
   if (n >= 5) asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else if (n >= 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// Direct-to-LDS loads (64 lanes x size bytes to the contiguous LDS bytes at
+// M0) written as inline assembly.  Issued through the compiler builtin, a
+// later LDS read cannot be told apart from the bytes a load in flight writes,
+// and the compiler makes it wait for every load in flight; here every
+// consumer waits explicitly instead (wait_vm_barrier), counting on the loads
+// of a wave completing in issue order.  The LDS address goes in M0, written
+// at least one instruction ahead of the load.
+__device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
+  return (uint32_t)(uintptr_t)MLAV_LDS(const void, ptr);
+}
+// row: wave-uniform global address; lane_off: this lane's byte offset from it
+__device__ __forceinline__ void dma16_row(const void* row, uint32_t lane_off, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(lane_off), "s"(row), "{m0}"(lds) : "memory");
+}
+// addr: this lane's global address
+__device__ __forceinline__ void dma16(const void* addr, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(addr), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* addr, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" :: "v"(addr), "{m0}"(lds) : "memory");
 }
 
 // Row reductions over the four lane groups that hold one query row (lanes
@@ -238,20 +296,19 @@ __device__ __forceinline__ float group_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-constexpr int kKRing = 6;                  // K operand reads in flight ahead of the S MFMAs
-constexpr int kVRing = 3;                  // V operand reads in flight ahead of the PV MFMAs
+constexpr int kKRing = 8;                  // K operand reads in flight ahead of the S MFMAs
 constexpr int kDvPerWave = kDv / kWaves;   // 128 dims of O per PV wave
 constexpr int kDtPerWave = kDvPerWave / 16;
 static_assert(kRowTiles == 1 && kWaves == 4, "four score waves of 16 rows, four PV waves");
-static_assert(kTilesPerIdx >= 4, "an index block outlasts the tile prefetch");
+static_assert(kTilesPerIdx >= 5, "an index block is loaded five tiles ahead of its first use");
 
 __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char s_v[kStages * kVSlotBytes];
   __shared__ __attribute__((aligned(16))) unsigned char s_r[kRopeSlots * kRopeSlotBytes];
-  __shared__ bf16x8 s_p[2][kWaves][2][64];      // P(i): buffer i % 2, row tile, hi/lo, lane
-  __shared__ int32_t s_idx[2][kIdxKeys];
-  __shared__ float s_alpha[2][kRowsPerItem];    // rescale factor of each row (valid when flagged)
-  __shared__ uint32_t s_rescale[2][kWaves];     // row tile rescaled at tile i
+  __shared__ bf16x8 s_p[2][kWaves][2][64];      // P(i) in buffer i & 1: row tile, hi/lo, lane
+  __shared__ __attribute__((aligned(16))) int32_t s_idx[2][kIdxKeys];   // slot blocks (double buffered)
+  __shared__ f32x4 s_alpha[2][16];              // [i & 1][n][rt]: rescale factor of row 16rt + n
+  __shared__ uint32_t s_rescale[2];             // byte rt != 0 when row tile rt rescaled
 
   // Work items of one key range sit on one XCD: workgroup b is dispatched to
   // XCD b % 8, so XCD x gets the contiguous items [x*per, (x+1)*per) and the
@@ -280,87 +337,108 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
   const int n = lane & 15, g = lane >> 4;
 
   const int r_local = 16 * r + n;
-  const bool trace = (p.flags & MLA_VERIFY_FLAG_TRACE_KEYS) && rb == 0;
-  const int64_t trace0 = (int64_t)kv0 + q0;
+  // this request's checked slots, prefix keys then tree nodes
+  const int32_t* kslots = p.slots + (kv0 + q0);
 
   // ---- slots: blocks of kIdxKeys keys staged in LDS (double buffered) ----
-  // threads 0..kIdxKeys-1 (the score waves) hold one key each.  load_idx only
-  // issues the index load; store_idx (a block later) checks the slot, records
-  // the trace and writes it to LDS, so the loads never hold up the tiles.
+  // The score waves copy the int32 slots of block b straight into LDS, lane
+  // = key, with the tile loads.  Keys past the range end re-read the range's
+  // last slot.  A slot of -1 (outside the pool) reads slot 0 instead and
+  // poisons the item: its rows become NaN.
   bool poison = false;
-  uint32_t idx_lo = 0, idx_hi = 0;
-  auto load_idx = [&](int blk) {
-    const int j = key0 + blk * kIdxKeys + tid;
-    const bool prefix = j < P;
-    const void* base = prefix ? p.kv_indices : p.out_cache_loc;
-    const int64_t at = prefix ? (int64_t)kv0 + j : (int64_t)q0 + (j - P);
-    const bool wide = prefix ? p.kv_idx64 : p.ocl_idx64;
-    uint32_t lo = 0, hi = 0;
-    if (j < key1) {
-      if (wide) {
-        const uint32_t* w = reinterpret_cast<const uint32_t*>(base) + 2 * at;
-        lo = w[0];
-        hi = w[1];
-      } else {
-        lo = reinterpret_cast<const uint32_t*>(base)[at];
-      }
-    }
-    idx_lo = lo;
-    idx_hi = hi;
+  auto issue_idx = [&](int blk) {
+    const int j = min(key0 + blk * kIdxKeys + 64 * wave + lane, key1 - 1);
+    dma4(kslots + j, lds_addr(&s_idx[blk & 1][64 * wave]));
   };
-  auto store_idx = [&](int blk) {
-    const int j = key0 + blk * kIdxKeys + tid;
-    const bool wide = j < P ? p.kv_idx64 : p.ocl_idx64;
-    const int64_t slot = wide ? (int64_t)(((uint64_t)idx_hi << 32) | idx_lo) : (int64_t)(int32_t)idx_lo;
-    int32_t v = 0;
-    if (j < key1) {
-      if (trace) p.trace[trace0 + j] = slot;
-      if (slot >= 0 && slot < p.num_slots) v = (int32_t)slot;
-      else poison = true;   // read slot 0 instead; the whole item's rows become NaN
-    }
-    s_idx[blk & 1][tid] = v;
-  };
-
   // ---- direct-to-LDS gather of tile t ----
   // wave w fetches the dims [0,512) of keys 4w..4w+3 (one 1 KB load per key,
   // lane = 16-byte unit); score wave w also fetches the rope rows of keys
   // 8w..8w+7 (one load).  Keys past the range end re-read the range's last
   // key (finite data, masked).  Loads per tile: 5 (score wave), 4 (PV wave).
-  auto issue = [&](int t) {
-    unsigned char* vslot = s_v + (t % kStages) * kVSlotBytes;
-    const int blk_first = key0 + (t / kTilesPerIdx) * kIdxKeys;
-    const int32_t* idx = s_idx[(t / kTilesPerIdx) & 1];
-    const int jt = key0 + t * kKeysPerTile;
+  // The slots of a tile are read from LDS one iteration before its loads are
+  // issued (read_slots), so the issue itself never waits on LDS.  Every key
+  // of a tile is a V key of exactly one wave, which checks it.
+  struct TileSlots {
+    int v[4];     // keys 4w..4w+3 (wave-uniform)
+    int rope;     // key 8w + lane / 8 (score waves)
+  };
+  auto read_slots = [&](int t) {
+    TileSlots ts;
+    const int blk = t / kTilesPerIdx;
+    const int32_t* idx = s_idx[blk & 1] - (key0 + blk * kIdxKeys);
+    const int j0 = key0 + t * kKeysPerTile + 4 * wave;            // this wave's first V key
+    // the V keys' slots in one 16-byte broadcast read (j0 is 4-aligned in
+    // the block), the rope key's per lane
+    const i32x4 v4 = *reinterpret_cast<const i32x4*>(idx + j0);
+    const int32_t rs = idx[min(j0 + 4 * wave + (lane >> 3), key1 - 1)];   // rope key 8w + lane / 8
+    int32_t any_bad = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int kk = 4 * wave + i;
-      // one key per load: the slot is wave-uniform, so the row address is
-      // formed on the scalar unit
-      const int slot = __builtin_amdgcn_readfirstlane(idx[min(jt + kk, key1 - 1) - blk_first]);
-      const uint16_t* row = p.kv_pool + (int64_t)slot * p.kv_row_stride;
-      __builtin_amdgcn_global_load_lds(row + (lane ^ vswz(kk)) * 8, MLAV_LDS(void, vslot + kk * kVStride),
-                                       16, 0, 0);
+      const int32_t v = __builtin_amdgcn_readfirstlane(v4[i]);
+      any_bad |= v;
+      ts.v[i] = max(v, 0);
     }
-    if (score_wave) {
-      unsigned char* rslot = s_r + (t % kRopeSlots) * kRopeSlotBytes;
-      const int kk = 8 * wave + (lane >> 3);
-      const int slot = idx[min(jt + kk, key1 - 1) - blk_first];
-      const uint16_t* row = p.kv_pool + (int64_t)slot * p.kv_row_stride;
-      const int unit = (lane & 7) ^ rswz(kk);
-      __builtin_amdgcn_global_load_lds(row + kDv + unit * 8, MLAV_LDS(void, rslot + (8 * wave) * 128), 16,
-                                       0, 0);
-    }
+    poison |= any_bad < 0;
+    ts.rope = score_wave ? max(rs, 0) : 0;
+    return ts;
+  };
+  const unsigned char* pool = reinterpret_cast<const unsigned char*>(p.kv_pool);
+  const uint32_t row_bytes = (uint32_t)p.kv_row_stride * 2;
+  // the loads of a tile one at a time, so that the roles can spread them
+  // over their MFMA steps
+  auto issue_key = [&](int t, const TileSlots& ts, int i) {
+    // one key per load: the slot is wave-uniform, so the row address is
+    // formed on the scalar unit
+    const int kk = 4 * wave + i;
+    const unsigned char* row = pool + (uint64_t)(uint32_t)ts.v[i] * row_bytes;
+    dma16_row(row, (uint32_t)(lane ^ vswz(kk)) * 16, lds_addr(s_v + (t % kStages) * kVSlotBytes + kk * kVStride));
+  };
+  auto issue_rope = [&](int t, const TileSlots& ts) {
+    const int kk = 8 * wave + (lane >> 3);
+    const unsigned char* row = pool + (uint64_t)(uint32_t)ts.rope * row_bytes;
+    const int unit = (lane & 7) ^ rswz(kk);
+    dma16(row + 2 * kDv + unit * 16, lds_addr(s_r + (t % kRopeSlots) * kRopeSlotBytes + (8 * wave) * 128));
+  };
+  auto issue = [&](int t, const TileSlots& ts) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) issue_key(t, ts, i);
+    if (score_wave) issue_rope(t, ts);
   };
   const int loads_per_tile = score_wave ? 5 : 4;
 
   // The two roles run separate loops with the same barrier sequence: one
-  // barrier before the first tile, then one per iteration i = 0..ntiles.
-  // Iteration i: scores of tile i (score waves) || PV of tile i - 1 (PV waves).
-  // Tile i + 2 goes to V slot (i + 2) % 4, last read by PV(i - 2), and to rope
-  // slot (i + 2) % 3, last read by the scores of tile i - 1.
-  auto top_of_iteration = [&](int i) {
-    wait_vm_barrier(i + 1 < ntiles ? loads_per_tile : 0);   // tile i landed
-    if (i + 2 < ntiles) issue(i + 2);
+  // barrier before the first tile, then one barrier A(i) at the top of each
+  // iteration i = 0..ntiles.  Iteration i: scores of tile i and P(i) into P
+  // buffer i & 1 (score waves) || PV of tile i - 1 from P buffer (i - 1) & 1
+  // and V^T(i) into registers (PV waves).  Tile i + 2 goes to the V and rope
+  // slots of tile i - 1, free since A(i); its slots were read from LDS in
+  // iteration i - 1.
+  // Index block b lands before tile 8b - 5 (issued after tile 8b - 6), and
+  // is first read with the slots of tile 8b in iteration 8b - 3; its buffer
+  // was last read in iteration 8b - 12.  The waits below count tile loads
+  // only: index loads in flight behind a tile make them wait a little longer,
+  // never less.
+  TileSlots next_slots{};
+  auto prologue = [&]() {
+    // nothing the compiler loaded may still be in flight once the loop runs
+    __builtin_amdgcn_s_waitcnt(0);
+    if (score_wave && ntiles > 0) issue_idx(0);
+    wait_vm_barrier(0);
+    for (int t = 0; t < 2 && t < ntiles; ++t) issue(t, read_slots(t));
+    if (2 < ntiles) next_slots = read_slots(2);
+  };
+  auto barrier_a = [&](int i) {
+    // tile i must have landed; tile i + 1 may still be in flight (the last
+    // wait takes everything)
+    if (i + 1 < ntiles) wait_vm_barrier(loads_per_tile);
+    else wait_vm_barrier(0);
+  };
+  // what iteration i issues after A(i): tile i + 2, index block i / 8 + 1
+  // (score waves, every 8th iteration) and the slots of tile i + 3
+  auto after_a = [&](int i) {
+    if (i + 2 < ntiles) issue(i + 2, next_slots);
+    if (score_wave && i % kTilesPerIdx == 0 && i + kTilesPerIdx < ntiles) issue_idx(i / kTilesPerIdx + 1);
+    if (i + 3 < ntiles) next_slots = read_slots(i + 3);
   };
 
   if (score_wave) {
@@ -393,50 +471,54 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
 
     // row tiles without rows contribute P = 0 and never rescale
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      s_p[b][r][0][lane] = bf16x8{};
-      s_p[b][r][1][lane] = bf16x8{};
-      if (lane == 0) s_rescale[b][r] = 0;
+    for (int bf = 0; bf < 2; ++bf) {
+      s_p[bf][r][0][lane] = bf16x8{};
+      s_p[bf][r][1][lane] = bf16x8{};
+      if (lane == 0) reinterpret_cast<uint8_t*>(&s_rescale[bf])[r] = 0;
     }
-    load_idx(0);
-    store_idx(0);
-    if (ntiles > kTilesPerIdx) load_idx(1);
-    wait_vm_barrier(0);
-    for (int t = 0; t < 2 && t < ntiles; ++t) issue(t);
+    prologue();
 
     for (int i = 0; i <= ntiles; ++i) {
-      top_of_iteration(i);
-      // index block b is first needed when tile 8b is issued (iteration 8b - 2)
-      if ((i + 3) % kTilesPerIdx == 0 && i + 3 < ntiles) {
-        const int blk = (i + 3) / kTilesPerIdx;
-        store_idx(blk);
-        if ((blk + 1) * kTilesPerIdx < ntiles) load_idx(blk + 1);
+      barrier_a(i);
+      if (!s_active || i >= ntiles) {
+        after_a(i);
+        continue;
       }
-      if (!s_active || i >= ntiles) continue;
+      const bool more = i + 2 < ntiles;
       const unsigned char* vslot = s_v + (i % kStages) * kVSlotBytes;
       const unsigned char* rslot = s_r + (i % kRopeSlots) * kRopeSlotBytes;
       const int jt = key0 + i * kKeysPerTile;
-      // S^T = K . Q^T: 32 keys x 16 rows, K-dim 576; operand reads run
-      // kKRing steps ahead of the MFMAs
+      // S^T = K . Q^T: 32 keys x 16 rows, K-dim 576.  The two 16-key halves
+      // alternate, so the two independent accumulator chains can issue back
+      // to back; operand reads run kKRing steps ahead of the MFMAs
       constexpr int kSSteps = 2 * (kDqk / 32);
       f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       auto k_operand = [&](int step) -> bf16x8 {
-        const int kt = step / (kDqk / 32), ks = step % (kDqk / 32);
+        const int kt = step & 1, ks = step >> 1;
         const unsigned char* ap = ks < 16 ? vslot + k_lo[ks & 3] + (ks >> 2) * 256 + 16 * kt * kVStride
                                           : rslot + 16 * kt * 128 + (ks == 16 ? r_off : r_off2);
         return *reinterpret_cast<const bf16x8*>(ap);
       };
+      // the scores gate the next PV step: their MFMAs go ahead of the PV
+      // wave's on this SIMD
+      __builtin_amdgcn_s_setprio(3);
       bf16x8 ka[kKRing];
 #pragma unroll
       for (int s = 0; s < kKRing; ++s) ka[s] = k_operand(s);
 #pragma unroll
       for (int step = 0; step < kSSteps; ++step) {
-        const int kt = step / (kDqk / 32), ks = step % (kDqk / 32);
+        const int kt = step & 1, ks = step >> 1;
         const bf16x8 a = ka[step % kKRing];
         if (step + kKRing < kSSteps) ka[step % kKRing] = k_operand(step + kKRing);
         sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], sacc[kt], 0, 0, 0);
+        // the tile loads of this iteration ride along with the MFMAs
+        if (step >= 1 && step <= 4 && more) issue_key(i + 2, next_slots, step - 1);
+        if (step == 5 && more) issue_rope(i + 2, next_slots);
+        if (step == 6 && i % kTilesPerIdx == 0 && i + kTilesPerIdx < ntiles) issue_idx(i / kTilesPerIdx + 1);
+        if (step == 8 && i + 3 < ntiles) next_slots = read_slots(i + 3);
         __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_setprio(0);
       // scores in base-2 units; mask the range tail and invisible tree keys
       const bool need_mask = jt + kKeysPerTile > min(P, key1);
       float mx = -INFINITY;
@@ -460,14 +542,13 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
       // exceeds it by more than 2^kRescaleSlack (then p <= 2^8 stays safe)
       const bool need = mx > m_run + kRescaleSlack;
       const bool any_need = __builtin_amdgcn_ballot_w64(need) != 0;
+      float alpha = 1.f;
       if (any_need) {
         const float m_new = need ? mx : m_run;
-        const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
         m_run = m_new;
-        if (g == 0) s_alpha[i & 1][r_local] = alpha;
       }
-      if (lane == 0) s_rescale[i & 1][r] = any_need;
       const float m_use = m_run == -INFINITY ? 0.f : m_run;
       float rs = 0.f;
       bf16x8 phi, plo;
@@ -485,6 +566,8 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
       l_run += group_sum(rs);
       s_p[i & 1][r][0][lane] = phi;
       s_p[i & 1][r][1][lane] = plo;
+      if (any_need && g == 0) s_alpha[i & 1][n][r] = alpha;
+      if (lane == 0) reinterpret_cast<uint8_t*>(&s_rescale[i & 1])[r] = any_need;
     }
     poison = __syncthreads_or(poison);
     if (poison && tid == 0) atomicOr(&p.hdr->err, (uint32_t)MLA_VERIFY_DEVERR_SLOT_RANGE);
@@ -511,49 +594,61 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
       for (int dt = 0; dt < kDtPerWave; ++dt)
         v_lo[dt] = v_key * kVStride + (n & 1) * 8 + (((16 * r + 2 * dt + ((n >> 1) & 1)) ^ vswz(v_key)) << 4);
     }
-    wait_vm_barrier(0);
-    for (int t = 0; t < 2 && t < ntiles; ++t) issue(t);
+    prologue();
+    // V^T of the tile the next PV step uses, in registers: v[dt] is the A
+    // operand for dims 128r + 16dt, keys kappa(g, 0..7)
+    bf16x8 v[kDtPerWave];
+    auto v_operand = [&](const unsigned char* vslot, int dt) -> bf16x8 {
+      const unsigned char* vb = vslot + v_lo[dt];
+      const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MLAV_LDS(i16x4, vb));
+      const i16x4 vc = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MLAV_LDS(i16x4, vb + 16 * kVStride));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vc, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
 
     for (int i = 0; i <= ntiles; ++i) {
-      top_of_iteration(i);
-      if (i == 0) continue;
-      // PV of tile i - 1 on this wave's 128 dims for every row tile.  Row
-      // tiles without rows carry P = 0, so the loop has no branches.
-      const int tp = i - 1;
-      const unsigned char* vslot = s_v + (tp % kStages) * kVSlotBytes;
+      barrier_a(i);
+      const unsigned char* vslot = s_v + (i % kStages) * kVSlotBytes;
+      if (i == 0) {
+#pragma unroll
+        for (int dt = 0; dt < kDtPerWave; ++dt) v[dt] = v_operand(vslot, dt);
+        after_a(i);
+        continue;
+      }
+      const bool more_dma = i + 2 < ntiles;
+      // P of every row tile, the rescale flags and the rescale factors in
+      // one LDS round trip
+      const int pb = (i - 1) & 1;
       bf16x8 ph[kWaves], pl[kWaves];
 #pragma unroll
       for (int rt = 0; rt < kWaves; ++rt) {
-        ph[rt] = s_p[tp & 1][rt][0][lane];
-        pl[rt] = s_p[tp & 1][rt][1][lane];
+        ph[rt] = s_p[pb][rt][0][lane];
+        pl[rt] = s_p[pb][rt][1][lane];
       }
-      const uint32_t* resc = s_rescale[tp & 1];
-      if ((resc[0] | resc[1] | resc[2] | resc[3]) != 0) {
+      const uint32_t resc = s_rescale[pb];
+      const f32x4 alpha4 = s_alpha[pb][n];
+      if (resc != 0) {
 #pragma unroll
         for (int rt = 0; rt < kWaves; ++rt) {
-          const float alpha = resc[rt] ? s_alpha[tp & 1][16 * rt + n] : 1.f;
+          const float alpha = ((resc >> (8 * rt)) & 0xffu) ? alpha4[rt] : 1.f;
 #pragma unroll
           for (int dt = 0; dt < kDtPerWave; ++dt) o[dt][rt] *= alpha;
         }
       }
-      auto v_operand = [&](int dt) -> bf16x8 {
-        const unsigned char* vb = vslot + v_lo[dt];
-        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MLAV_LDS(i16x4, vb));
-        const i16x4 vc = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MLAV_LDS(i16x4, vb + 16 * kVStride));
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vc, 0, 1, 2, 3, 4, 5, 6, 7));
-      };
-      bf16x8 va_ring[kVRing];
-#pragma unroll
-      for (int s = 0; s < kVRing; ++s) va_ring[s] = v_operand(s);
+      // PV of tile i - 1 (row tiles without rows carry P = 0, so the loop has
+      // no branches); each operand, once used, is replaced by V^T(i)
+      const bool more = i < ntiles;
 #pragma unroll
       for (int dt = 0; dt < kDtPerWave; ++dt) {
-        const bf16x8 a = va_ring[dt % kVRing];
-        if (dt + kVRing < kDtPerWave) va_ring[dt % kVRing] = v_operand(dt + kVRing);
+        const bf16x8 a = v[dt];
 #pragma unroll
         for (int rt = 0; rt < kWaves; ++rt) {
           o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph[rt], o[dt][rt], 0, 0, 0);
           o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[rt], o[dt][rt], 0, 0, 0);
         }
+        if (more) v[dt] = v_operand(vslot, dt);
+        // the tile loads of this iteration ride along with the MFMAs
+        if (dt < 4 && more_dma) issue_key(i + 2, next_slots, dt);
+        if (dt == 5 && i + 3 < ntiles) next_slots = read_slots(i + 3);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -680,8 +775,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(KernelParams p) {
 
 // ---------------------------------------------------------------------------
 int launch_meta(const KernelParams& p, const mla_verify_layout_t& lay, void* stream) {
-  (void)lay;
-  hipLaunchKernelGGL(meta_kernel, dim3(1), dim3(kMetaThreads), 0, (hipStream_t)stream, p);
+  hipLaunchKernelGGL(meta_kernel, dim3(lay.meta_grid), dim3(kMetaThreads), 0, (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
 

@@ -24,7 +24,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert {"mla_verify_plan", "mla_verify_workspace_size", "mla_verify_run"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.mla_verify_abi_version() == 1
+    assert lib.mla_verify_abi_version() == 2
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -74,6 +74,11 @@ def test_plan_layout_arithmetic():
     assert lay.total_bytes >= lay.partial_ml_offset + lay.item_capacity * rows * 8
     assert B.workspace_size(p) == lay.total_bytes
     assert lay.trace_offset == 0
+    # staged int32 slots of every key position, after the other regions
+    assert lay.slots_offset % 256 == 0 and lay.slots_offset >= lay.partial_ml_offset
+    assert lay.total_bytes >= lay.slots_offset + (1_480_000 + 512) * 4
+    assert lay.meta_grid == 1 + 256
+    assert B.layout(_plan(max_kv_tokens=1000, max_q_tokens=24)).meta_grid == 2
     t = B.layout(_plan(flags=B.FLAG_TRACE_KEYS))
     assert t.trace_offset % 256 == 0 and t.total_bytes >= t.trace_offset + (1_480_000 + 512) * 8
     # explicit target overrides the CU count

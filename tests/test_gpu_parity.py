@@ -32,6 +32,13 @@ def _check_metadata(inst, v, rec):
             base = int(inst.kv_indptr[b]) + int(inst.qo_indptr[b])
             keys = rec["keys"][b]
             assert np.array_equal(tr[base:base + len(keys)], keys), f"request {b}"
+    # staged slots: every request's combined key list, -1 where a slot is outside the pool
+    sl = v.region(lay.slots_offset, max(total_kv + total_q, 1), torch.int32).cpu().numpy()
+    for b in range(inst.batch):
+        base = int(inst.kv_indptr[b]) + int(inst.qo_indptr[b])
+        keys = np.asarray(rec["keys"][b], np.int64)
+        want = np.where((keys >= 0) & (keys < inst.num_slots), keys, -1).astype(np.int32)
+        assert np.array_equal(sl[base:base + len(keys)], want), f"staged slots of request {b}"
     items = v.region(lay.items_offset, max(n_items, 1) * 8, torch.int32).cpu().numpy().reshape(-1, 8)
     items = items[:n_items]
     rows_per = lay.rows_per_item
