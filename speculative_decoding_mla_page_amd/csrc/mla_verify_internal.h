@@ -16,7 +16,8 @@ constexpr int kRowsPerWave = 16 * kRowTiles;
 constexpr int kRowsPerItem = kWaves * kRowsPerWave;  // query rows per work item
 constexpr int kStages = 3;                 // LDS slots of key tiles (V part)
 constexpr int kIdxKeys = 256;              // slots staged per index block (8 tiles)
-constexpr int kPartialThreads = 2 * kWaves * 64;   // score waves + PV waves
+constexpr int kPVWaves = 8;                // PV waves per workgroup (64 output dims each)
+constexpr int kPartialThreads = (kWaves + kPVWaves) * 64;   // score waves + PV waves
 constexpr int kMetaThreads = 256;
 constexpr int kMetaKeysPerGroup = 1024;    // slot-staging workgroups: one per this many keys of capacity
 constexpr int kMetaStageGroups = 256;      // ... and at most this many

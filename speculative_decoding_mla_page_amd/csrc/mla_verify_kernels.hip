@@ -24,6 +24,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "mla_verify_internal.h"
 
 namespace mlav {
@@ -232,18 +234,17 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// split partial: one workgroup of 8 waves per work item (64 query rows x one
-// key range), specialised in two roles that run side by side on each SIMD:
+// split partial: one workgroup of 12 waves per work item (64 query rows x one
+// key range), specialised in two roles that run side by side on each SIMD
+// (one score wave and two PV waves per SIMD):
 //   score waves 0-3: wave r owns query rows 16r..16r+15 (one 16-row MFMA
 //     tile); for tile i it forms S^T = K . Q^T, keeps the online softmax of
 //     its rows and publishes P(i) = hi + lo and the rows' rescale factors.
-//   PV waves 4-7: wave 4+r owns dims [128r, 128r+128) of O for all 64 rows;
+//   PV waves 4-11: wave 4+r owns dims [64r, 64r+64) of O for all 64 rows;
 //     during tile i it accumulates O^T += V^T . P^T for tile i-1 and moves
-//     its quarter of V^T(i) from LDS (transpose load) into registers.
-// Each iteration has two barriers: A (tile i has landed; P(i-1) is ready)
-// and B (the PV waves hold P(i-1) in registers, so the score waves may
-// overwrite it with P(i)).  Tile i's LDS slot is free once A(i+1) passes,
-// so three tiles stay in flight.
+//     its eighth of V^T(i) from LDS (transpose load) into registers.
+// One barrier per tile (A(i): tile i has landed, P(i-1) is ready); P is
+// double buffered.
 // ---------------------------------------------------------------------------
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 #define MLAV_LDS(T, ptr) ((__attribute__((address_space(3))) T*)(ptr))
@@ -252,10 +253,10 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 // flight (direct-to-LDS loads complete in issue order and count here), finish
 // this wave's LDS operations, then meet the other waves.  The memory clobber
 // keeps the compiler from moving LDS accesses across the barrier.  n is one
-// of 0, 4, 5 (one tile of 4 or 5 loads).
+// of 0, 1, 4 (one tile of 1 or 4 loads).
 __device__ __forceinline__ void wait_vm_barrier(int n) {
-  if (n >= 5) asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if (n >= 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (n >= 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if (n >= 1) asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 // Direct-to-LDS loads (64 lanes x size bytes to the contiguous LDS bytes at
@@ -297,9 +298,10 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 
 constexpr int kKRing = 8;                  // K operand reads in flight ahead of the S MFMAs
-constexpr int kDvPerWave = kDv / kWaves;   // 128 dims of O per PV wave
+constexpr int kDvPerWave = kDv / kPVWaves;   // 64 dims of O per PV wave
 constexpr int kDtPerWave = kDvPerWave / 16;
-static_assert(kRowTiles == 1 && kWaves == 4, "four score waves of 16 rows, four PV waves");
+static_assert(kRowTiles == 1 && kWaves == 4 && kPVWaves == 8, "four score waves of 16 rows, eight PV waves");
+static_assert(kPVWaves * 4 == kKeysPerTile, "each PV wave gathers four keys of a tile");
 static_assert(kTilesPerIdx >= 5, "an index block is loaded five tiles ahead of its first use");
 
 __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParams p) {
@@ -333,7 +335,7 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool score_wave = wave < kWaves;
-  const int r = wave & (kWaves - 1);            // row tile (score) or dim quarter (PV)
+  const int r = score_wave ? wave : wave - kWaves;   // row tile (score) or dim eighth (PV)
   const int n = lane & 15, g = lane >> 4;
 
   const int r_local = 16 * r + n;
@@ -351,35 +353,41 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
     dma4(kslots + j, lds_addr(&s_idx[blk & 1][64 * wave]));
   };
   // ---- direct-to-LDS gather of tile t ----
-  // wave w fetches the dims [0,512) of keys 4w..4w+3 (one 1 KB load per key,
-  // lane = 16-byte unit); score wave w also fetches the rope rows of keys
+  // PV wave r fetches the dims [0,512) of keys 4r..4r+3 (one 1 KB load per
+  // key, lane = 16-byte unit); score wave w fetches the rope rows of keys
   // 8w..8w+7 (one load).  Keys past the range end re-read the range's last
-  // key (finite data, masked).  Loads per tile: 5 (score wave), 4 (PV wave).
+  // key (finite data, masked).  Loads per tile: 1 (score wave), 4 (PV wave).
   // The slots of a tile are read from LDS one iteration before its loads are
   // issued (read_slots), so the issue itself never waits on LDS.  Every key
-  // of a tile is a V key of exactly one wave, which checks it.
+  // of a tile is a V key of exactly one PV wave, which checks it.
   struct TileSlots {
-    int v[4];     // keys 4w..4w+3 (wave-uniform)
+    int v[4];     // keys 4r..4r+3 (PV waves, wave-uniform)
     int rope;     // key 8w + lane / 8 (score waves)
   };
   auto read_slots = [&](int t) {
     TileSlots ts;
     const int blk = t / kTilesPerIdx;
     const int32_t* idx = s_idx[blk & 1] - (key0 + blk * kIdxKeys);
-    const int j0 = key0 + t * kKeysPerTile + 4 * wave;            // this wave's first V key
-    // the V keys' slots in one 16-byte broadcast read (j0 is 4-aligned in
-    // the block), the rope key's per lane
-    const i32x4 v4 = *reinterpret_cast<const i32x4*>(idx + j0);
-    const int32_t rs = idx[min(j0 + 4 * wave + (lane >> 3), key1 - 1)];   // rope key 8w + lane / 8
-    int32_t any_bad = 0;
+    const int jt = key0 + t * kKeysPerTile;
+    if (score_wave) {
+      // the rope key's slot, per lane
+      ts.rope = max(idx[min(jt + 8 * wave + (lane >> 3), key1 - 1)], 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int32_t v = __builtin_amdgcn_readfirstlane(v4[i]);
-      any_bad |= v;
-      ts.v[i] = max(v, 0);
+      for (int i = 0; i < 4; ++i) ts.v[i] = 0;
+    } else {
+      // the V keys' slots in one 16-byte broadcast read (4r is 4-aligned
+      // in the block)
+      const i32x4 v4 = *reinterpret_cast<const i32x4*>(idx + jt + 4 * r);
+      int32_t any_bad = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int32_t v = __builtin_amdgcn_readfirstlane(v4[i]);
+        any_bad |= v;
+        ts.v[i] = max(v, 0);
+      }
+      poison |= any_bad < 0;
+      ts.rope = 0;
     }
-    poison |= any_bad < 0;
-    ts.rope = score_wave ? max(rs, 0) : 0;
     return ts;
   };
   const unsigned char* pool = reinterpret_cast<const unsigned char*>(p.kv_pool);
@@ -389,7 +397,7 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
   auto issue_key = [&](int t, const TileSlots& ts, int i) {
     // one key per load: the slot is wave-uniform, so the row address is
     // formed on the scalar unit
-    const int kk = 4 * wave + i;
+    const int kk = 4 * r + i;
     const unsigned char* row = pool + (uint64_t)(uint32_t)ts.v[i] * row_bytes;
     dma16_row(row, (uint32_t)(lane ^ vswz(kk)) * 16, lds_addr(s_v + (t % kStages) * kVSlotBytes + kk * kVStride));
   };
@@ -400,17 +408,22 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
     dma16(row + 2 * kDv + unit * 16, lds_addr(s_r + (t % kRopeSlots) * kRopeSlotBytes + (8 * wave) * 128));
   };
   auto issue = [&](int t, const TileSlots& ts) {
+    if (score_wave) {
+      issue_rope(t, ts);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) issue_key(t, ts, i);
-    if (score_wave) issue_rope(t, ts);
+      for (int i = 0; i < 4; ++i) issue_key(t, ts, i);
+    }
   };
-  const int loads_per_tile = score_wave ? 5 : 4;
+  const int loads_per_tile = score_wave ? 1 : 4;
 
   // The two roles run separate loops with the same barrier sequence: one
   // barrier before the first tile, then one barrier A(i) at the top of each
-  // iteration i = 0..ntiles.  Iteration i: scores of tile i and P(i) into P
-  // buffer i & 1 (score waves) || PV of tile i - 1 from P buffer (i - 1) & 1
-  // and V^T(i) into registers (PV waves).  Tile i + 2 goes to the V and rope
+  // iteration i = 0..ntiles + 1.  Iteration i: scores of tile i and P(i) into
+  // P buffer i & 1 (score waves) || PV of tile i - 2 from registers, P(i - 1)
+  // out of P buffer (i - 1) & 1 and V^T(i) into registers (PV waves).  P(i - 1)
+  // is read in iteration i, before the score waves rewrite its buffer in
+  // iteration i + 1.  Tile i + 2 goes to the V and rope
   // slots of tile i - 1, free since A(i); its slots were read from LDS in
   // iteration i - 1.
   // Index block b lands before tile 8b - 5 (issued after tile 8b - 6), and
@@ -422,7 +435,6 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
   auto prologue = [&]() {
     // nothing the compiler loaded may still be in flight once the loop runs
     __builtin_amdgcn_s_waitcnt(0);
-    if (score_wave && ntiles > 0) issue_idx(0);
     wait_vm_barrier(0);
     for (int t = 0; t < 2 && t < ntiles; ++t) issue(t, read_slots(t));
     if (2 < ntiles) next_slots = read_slots(2);
@@ -445,6 +457,8 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
     // ---- score waves: query rows 16r + n; rows are (node, head), heads fastest
     const bool row_ok = r_local < nrows;
     const bool s_active = r < nrt;
+    // the first slot block is on its way while the queries load
+    if (ntiles > 0) issue_idx(0);
     bf16x8 qf[kDqk / 32];
     uint64_t anc;
     {
@@ -478,7 +492,7 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
     }
     prologue();
 
-    for (int i = 0; i <= ntiles; ++i) {
+    for (int i = 0; i <= ntiles + 1; ++i) {
       barrier_a(i);
       if (!s_active || i >= ntiles) {
         after_a(i);
@@ -499,8 +513,8 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
                                           : rslot + 16 * kt * 128 + (ks == 16 ? r_off : r_off2);
         return *reinterpret_cast<const bf16x8*>(ap);
       };
-      // the scores gate the next PV step: their MFMAs go ahead of the PV
-      // wave's on this SIMD
+      // the scores and P gate the next PV step: the score wave goes ahead of
+      // the PV wave on this SIMD until P is written
       __builtin_amdgcn_s_setprio(3);
       bf16x8 ka[kKRing];
 #pragma unroll
@@ -512,13 +526,11 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
         if (step + kKRing < kSSteps) ka[step % kKRing] = k_operand(step + kKRing);
         sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], sacc[kt], 0, 0, 0);
         // the tile loads of this iteration ride along with the MFMAs
-        if (step >= 1 && step <= 4 && more) issue_key(i + 2, next_slots, step - 1);
-        if (step == 5 && more) issue_rope(i + 2, next_slots);
+        if (step == 2 && more) issue_rope(i + 2, next_slots);
         if (step == 6 && i % kTilesPerIdx == 0 && i + kTilesPerIdx < ntiles) issue_idx(i / kTilesPerIdx + 1);
         if (step == 8 && i + 3 < ntiles) next_slots = read_slots(i + 3);
         __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_s_setprio(0);
       // scores in base-2 units; mask the range tail and invisible tree keys
       const bool need_mask = jt + kKeysPerTile > min(P, key1);
       float mx = -INFINITY;
@@ -568,6 +580,7 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
       s_p[i & 1][r][1][lane] = plo;
       if (any_need && g == 0) s_alpha[i & 1][n][r] = alpha;
       if (lane == 0) reinterpret_cast<uint8_t*>(&s_rescale[i & 1])[r] = any_need;
+      __builtin_amdgcn_s_setprio(0);
     }
     poison = __syncthreads_or(poison);
     if (poison && tid == 0) atomicOr(&p.hdr->err, (uint32_t)MLA_VERIFY_DEVERR_SLOT_RANGE);
@@ -577,80 +590,107 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
       pm[1] = poison ? NAN : l_run;
     }
   } else {
-    // ---- PV waves: O for all 64 rows, dims [128r, 128r + 128); o[dt][rt]
-    // holds, in lane (g, n), O[row 16rt + n][dim 128r + 16dt + 4g + i]
+    // ---- PV waves: O for all 64 rows, dims [64r, 64r + 64); o[dt][rt]
+    // holds, in lane (g, n), O[row 16rt + n][dim 64r + 16dt + 4g + i]
     f32x4 o[kDtPerWave][kWaves];
 #pragma unroll
     for (int dt = 0; dt < kDtPerWave; ++dt)
 #pragma unroll
       for (int rt = 0; rt < kWaves; ++rt) o[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
     //   V^T (A operand, transposed read): lane s = 4k + j of group g points at
-    //   key 4g + k (and 16 + 4g + k), dims 128r + 16dt + 4j, i.e. unit
-    //   16r + 2dt + (j >> 1), byte 8 (j & 1)
+    //   key 4g + k (and 16 + 4g + k), dims 64r + 16dt + 4j, i.e. unit
+    //   8r + 2dt + (j >> 1), byte 8 (j & 1)
     int v_lo[kDtPerWave];
     {
       const int v_key = 4 * g + (n >> 2);
 #pragma unroll
       for (int dt = 0; dt < kDtPerWave; ++dt)
-        v_lo[dt] = v_key * kVStride + (n & 1) * 8 + (((16 * r + 2 * dt + ((n >> 1) & 1)) ^ vswz(v_key)) << 4);
+        v_lo[dt] = v_key * kVStride + (n & 1) * 8 + ((((kDvPerWave / 8) * r + 2 * dt + ((n >> 1) & 1)) ^ vswz(v_key)) << 4);
     }
     prologue();
-    // V^T of the tile the next PV step uses, in registers: v[dt] is the A
-    // operand for dims 128r + 16dt, keys kappa(g, 0..7)
-    bf16x8 v[kDtPerWave];
+    // The PV waves run two tiles behind the score waves: iteration i
+    // multiplies tile i - 2 with operands that are all in registers by then
+    // (P(i - 2) and its rescale factors, read in iteration i - 1; V^T(i - 2),
+    // read in iteration i - 2), and meanwhile reads P(i - 1) and V^T(i).
+    // vt[s][dt] is the A operand for dims 64r + 16dt, keys kappa(g, 0..7), of
+    // the tile with parity s.
+    bf16x8 vt[2][kDtPerWave];
+    bf16x8 ph[kWaves], pl[kWaves];
+    uint32_t resc = 0;
+    f32x4 alpha4 = f32x4{1.f, 1.f, 1.f, 1.f};
     auto v_operand = [&](const unsigned char* vslot, int dt) -> bf16x8 {
       const unsigned char* vb = vslot + v_lo[dt];
       const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MLAV_LDS(i16x4, vb));
       const i16x4 vc = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MLAV_LDS(i16x4, vb + 16 * kVStride));
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vc, 0, 1, 2, 3, 4, 5, 6, 7));
     };
+    auto read_p = [&](int t, int rt) {   // P(t) of row tile rt
+      ph[rt] = s_p[t & 1][rt][0][lane];
+      pl[rt] = s_p[t & 1][rt][1][lane];
+    };
 
-    for (int i = 0; i <= ntiles; ++i) {
+    // one iteration; the parity of i is a compile-time constant so that the
+    // two V^T register sets are addressed statically
+    auto pv_iteration = [&](int i, auto parity) {
+      constexpr int sv = decltype(parity)::value;   // = i & 1: V^T(i - 2) in, V^T(i) out
       barrier_a(i);
       const unsigned char* vslot = s_v + (i % kStages) * kVSlotBytes;
-      if (i == 0) {
+      const bool v_next = i < ntiles;              // V^T(i) to read
+      const bool p_next = i >= 1 && i <= ntiles;   // P(i - 1) to read
+      if (i < 2) {
+        if (v_next) {
 #pragma unroll
-        for (int dt = 0; dt < kDtPerWave; ++dt) v[dt] = v_operand(vslot, dt);
+          for (int dt = 0; dt < kDtPerWave; ++dt) vt[sv][dt] = v_operand(vslot, dt);
+        }
+        if (p_next) {
+          resc = s_rescale[(i - 1) & 1];
+          alpha4 = s_alpha[(i - 1) & 1][n];
+#pragma unroll
+          for (int rt = 0; rt < kWaves; ++rt) read_p(i - 1, rt);
+        }
         after_a(i);
-        continue;
+        return;
       }
       const bool more_dma = i + 2 < ntiles;
-      // P of every row tile, the rescale flags and the rescale factors in
-      // one LDS round trip
-      const int pb = (i - 1) & 1;
-      bf16x8 ph[kWaves], pl[kWaves];
+      const bool more_slots = i + 3 < ntiles;
+      const uint32_t resc_cur = resc;
+      const f32x4 alpha_cur = alpha4;
+      if (p_next) {
+        resc = s_rescale[(i - 1) & 1];
+        alpha4 = s_alpha[(i - 1) & 1][n];
+      }
+      // PV of tile i - 2, one row tile at a time (row tiles without rows
+      // carry P = 0, so there are no branches but the rare rescale); each P
+      // operand, once used, is replaced by P(i - 1), and in the last pass
+      // each V^T operand by V^T(i)
 #pragma unroll
       for (int rt = 0; rt < kWaves; ++rt) {
-        ph[rt] = s_p[pb][rt][0][lane];
-        pl[rt] = s_p[pb][rt][1][lane];
-      }
-      const uint32_t resc = s_rescale[pb];
-      const f32x4 alpha4 = s_alpha[pb][n];
-      if (resc != 0) {
-#pragma unroll
-        for (int rt = 0; rt < kWaves; ++rt) {
-          const float alpha = ((resc >> (8 * rt)) & 0xffu) ? alpha4[rt] : 1.f;
+        if ((resc_cur >> (8 * rt)) & 0xffu) {
+          const float alpha = alpha_cur[rt];
 #pragma unroll
           for (int dt = 0; dt < kDtPerWave; ++dt) o[dt][rt] *= alpha;
         }
-      }
-      // PV of tile i - 1 (row tiles without rows carry P = 0, so the loop has
-      // no branches); each operand, once used, is replaced by V^T(i)
-      const bool more = i < ntiles;
 #pragma unroll
-      for (int dt = 0; dt < kDtPerWave; ++dt) {
-        const bf16x8 a = v[dt];
+        for (int dt = 0; dt < kDtPerWave; ++dt)
+          o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[sv][dt], ph[rt], o[dt][rt], 0, 0, 0);
 #pragma unroll
-        for (int rt = 0; rt < kWaves; ++rt) {
-          o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ph[rt], o[dt][rt], 0, 0, 0);
-          o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pl[rt], o[dt][rt], 0, 0, 0);
+        for (int dt = 0; dt < kDtPerWave; ++dt) {
+          o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[sv][dt], pl[rt], o[dt][rt], 0, 0, 0);
+          if (rt == kWaves - 1 && v_next) vt[sv][dt] = v_operand(vslot, dt);
         }
-        if (more) v[dt] = v_operand(vslot, dt);
+        if (p_next) read_p(i - 1, rt);
         // the tile loads of this iteration ride along with the MFMAs
-        if (dt < 4 && more_dma) issue_key(i + 2, next_slots, dt);
-        if (dt == 5 && i + 3 < ntiles) next_slots = read_slots(i + 3);
+        if (rt == 1 && more_dma) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) issue_key(i + 2, next_slots, k);
+        }
+        if (rt == 2 && more_slots) next_slots = read_slots(i + 3);
         __builtin_amdgcn_sched_barrier(0);
       }
+    };
+    for (int i = 0; i <= ntiles + 1; i += 2) {
+      pv_iteration(i, std::integral_constant<int, 0>{});
+      if (i + 1 <= ntiles + 1) pv_iteration(i + 1, std::integral_constant<int, 1>{});
     }
     poison = __syncthreads_or(poison);
 #pragma unroll
