@@ -110,6 +110,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-calls", type=int, default=20,
                     help="extra calls each preceded by a 1 GiB cache scrub (reported, not the value)")
+    ap.add_argument("--fused-save-calls", type=int, default=50,
+                    help="extra calls that also store the draft rows into the pool (reported, not the value)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (a known-size "
                          "kernel for scaling hardware byte counters)")
@@ -193,6 +195,35 @@ def main():
         cold_us = float(np.median([e[0].elapsed_time(e[1]) for e in ce]) * 1e3)
         del scrub
 
+    # the same call with the fused KV save: the draft rows are handed over and
+    # stored at out_cache_loc by the metadata launch (same values, so the pool
+    # is unchanged); timed over its own loop, not the value
+    fused = None
+    if args.fused_save_calls > 0:
+        ocl = di.out_cache_loc[:di.total_q].to(torch.int64)
+        kv_new = di.pool[ocl][:, :576].contiguous()
+        a2 = B.make_args(di.batch, di.sm_scale, di.q, di.pool, di.qo_indptr, di.kv_indptr,
+                         di.kv_indices, di.out_cache_loc, di.custom_mask, di.mask_indptr,
+                         out, lse, num_slots=di.num_slots, kv_new=kv_new)
+        for _ in range(5):
+            B.run(ver.plan, a2, ver.workspace, sp)
+        fe = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.fused_save_calls)]
+        for e in fe:
+            e[0].record(stream)
+            B.run_phase(ver.plan, a2, ver.workspace, B.PHASE_META, sp)
+            e[1].record(stream)
+            B.run_phase(ver.plan, a2, ver.workspace, B.PHASE_PARTIAL, sp)
+            B.run_phase(ver.plan, a2, ver.workspace, B.PHASE_MERGE, sp)
+        fe_all = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        fe_all[0].record(stream)
+        for _ in range(args.fused_save_calls):
+            B.run(ver.plan, a2, ver.workspace, sp)
+        fe_all[1].record(stream)
+        torch.cuda.synchronize()
+        fused = {"us_per_call": fe_all[0].elapsed_time(fe_all[1]) * 1e3 / args.fused_save_calls,
+                 "meta_us": float(np.median([e[0].elapsed_time(e[1]) for e in fe]) * 1e3),
+                 "rows_saved": int(di.total_q), "calls": args.fused_save_calls}
+
     # reference numbers: the same call checked for the device error word
     if ver.error_word() != 0:
         raise RuntimeError(f"device error word {ver.error_word():#x}")
@@ -236,6 +267,7 @@ def main():
                                            flops / (PEAK_MFMA_BF16_TFLOPS * 1e12)) * 1e6,
                           "frac": max(kv_bytes / (PEAK_HBM_GBS * 1e9),
                                       flops / (PEAK_MFMA_BF16_TFLOPS * 1e12)) / (us_call * 1e-6)},
+        "fused_kv_save": fused,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MLA_VERIFY_ABI_VERSION 2
+#define MLA_VERIFY_ABI_VERSION 3
 #define MLA_VERIFY_D_QK 576          /* latent width used by Q.K^T (512 + 64 rope) */
 #define MLA_VERIFY_D_V 512           /* V = latent dims [0, 512) */
 #define MLA_VERIFY_MAX_TREE_NODES 64 /* tree visibility is packed into one 64-bit word */
@@ -129,6 +129,15 @@ typedef struct {
  *                 16-byte aligned, strides multiples of 4.
  *   lse           fp32 [sum T, H] at lse + t*lse_stride_tok + h, natural-log
  *                 log-sum-exp of the scaled visible scores; may be NULL.
+ *   kv_new        bf16 [sum T, >= 576] at kv_new + t*kv_new_stride_tok, or NULL.
+ *                 When given, the call first stores row t (576 values) into
+ *                 the pool at slot out_cache_loc[t] (the KV save of this
+ *                 step's draft tokens, fused into the metadata launch), so the
+ *                 pool must be writable and those slots distinct; rows whose
+ *                 slot lies outside the pool are not stored (the slot range
+ *                 error is raised as for any gathered slot).  16-byte aligned,
+ *                 stride a multiple of 8.  When NULL the rows must already be
+ *                 in the pool.
  * A row that sees no key (P_b = 0 and an all-zero mask row) gets out = 0 and
  * lse = -inf.  Key order within a request is the prefix, then the tree nodes;
  * a slot listed twice is two keys.  Scores are sm_scale * (q . k).
@@ -153,6 +162,8 @@ typedef struct {
   int64_t out_stride_head;
   float* lse;
   int64_t lse_stride_tok;
+  const void* kv_new;          /* optional: draft rows to store at out_cache_loc first */
+  int64_t kv_new_stride_tok;
 } mla_verify_args_t;
 
 /* Where each workspace region lives (byte offsets from the workspace base,

@@ -77,6 +77,8 @@ class Args(ctypes.Structure):
         ("out_stride_head", ctypes.c_int64),
         ("lse", ctypes.c_void_p),
         ("lse_stride_tok", ctypes.c_int64),
+        ("kv_new", ctypes.c_void_p),
+        ("kv_new_stride_tok", ctypes.c_int64),
     ]
 
 
@@ -191,7 +193,8 @@ def _ptr(t) -> int:
 
 
 def make_args(batch_size: int, sm_scale: float, q, kv_pool, qo_indptr, kv_indptr, kv_indices,
-              out_cache_loc, custom_mask, mask_indptr, out, lse=None, num_slots: Optional[int] = None) -> Args:
+              out_cache_loc, custom_mask, mask_indptr, out, lse=None, num_slots: Optional[int] = None,
+              kv_new=None) -> Args:
     """Build the argument struct from torch tensors (bf16 q/pool may be int16 or
     bfloat16 views; strides are read from the tensors)."""
     a = Args()
@@ -214,6 +217,8 @@ def make_args(batch_size: int, sm_scale: float, q, kv_pool, qo_indptr, kv_indptr
     a.out_stride_head = out.stride(1)
     a.lse = _ptr(lse)
     a.lse_stride_tok = lse.stride(0) if lse is not None else 0
+    a.kv_new = _ptr(kv_new)
+    a.kv_new_stride_tok = kv_new.stride(0) if kv_new is not None else 0
     return a
 
 

@@ -46,6 +46,9 @@ mla_verify_status_t check_args(const PlanImpl& pl, const mla_verify_args_t* a, c
     return MLA_VERIFY_ERR_INVALID_ARGUMENT;
   if (a->lse && (!aligned(a->lse, 4) || a->lse_stride_tok <= 0))
     return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  // 16-byte row copies of the draft rows into the pool
+  if (a->kv_new && (!aligned(a->kv_new, 16) || a->kv_new_stride_tok < kDqk || a->kv_new_stride_tok % 8))
+    return MLA_VERIFY_ERR_INVALID_ARGUMENT;
   if (!aligned(a->qo_indptr, 4) || !aligned(a->kv_indptr, 4) || !aligned(a->mask_indptr, 4))
     return MLA_VERIFY_ERR_INVALID_ARGUMENT;
   if (!aligned(a->kv_indices, c.kv_indices_dtype == MLA_VERIFY_I64 ? 8 : 4) ||
@@ -82,6 +85,8 @@ KernelParams make_params(const PlanImpl& pl, const mla_verify_args_t* a, void* w
   p.out_stride_head = a->out_stride_head;
   p.lse = a->lse;
   p.lse_stride_tok = a->lse_stride_tok;
+  p.kv_new = reinterpret_cast<const uint16_t*>(a->kv_new);
+  p.kv_new_stride_tok = a->kv_new_stride_tok;
   p.kv_idx64 = c.kv_indices_dtype == MLA_VERIFY_I64;
   p.ocl_idx64 = c.out_cache_loc_dtype == MLA_VERIFY_I64;
   p.max_q_tokens = c.max_q_tokens;

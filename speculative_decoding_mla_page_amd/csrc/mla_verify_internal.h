@@ -75,6 +75,8 @@ struct KernelParams {
   int64_t out_stride_head;
   float* lse;
   int64_t lse_stride_tok;
+  const uint16_t* kv_new;       // optional draft rows stored into the pool by the metadata launch
+  int64_t kv_new_stride_tok;
   // plan
   int32_t kv_idx64;
   int32_t ocl_idx64;

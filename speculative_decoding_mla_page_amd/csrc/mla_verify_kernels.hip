@@ -102,11 +102,35 @@ __device__ void stage_slots(const KernelParams& p, int group, int groups) {
 }
 
 // ---------------------------------------------------------------------------
+// fused KV save (metadata launch, the slot-staging workgroups): draft token
+// t's latent row kv_new[t] goes to pool slot out_cache_loc[t], 16 bytes per
+// thread (72 per row), before the partial launch gathers it.  Only tokens of
+// the checked range [0, qo_indptr[B]) and slots inside the pool are stored.
+// ---------------------------------------------------------------------------
+constexpr int kRowUnits = kDqk * 2 / 16;   // 16-byte units per latent row
+__device__ void save_rows(const KernelParams& p, int group, int groups) {
+  const int B = p.batch;
+  if (B <= 0 || p.kv_new == nullptr) return;
+  const int qB = p.qo_indptr[B];
+  if (qB <= 0 || qB > p.max_q_tokens) return;
+  uint16_t* pool = const_cast<uint16_t*>(p.kv_pool);
+  const int64_t units = (int64_t)qB * kRowUnits;
+  for (int64_t u = (int64_t)group * kMetaThreads + threadIdx.x; u < units; u += (int64_t)groups * kMetaThreads) {
+    const int t = (int)(u / kRowUnits), c = (int)(u % kRowUnits);
+    const int64_t slot = load_index(p.out_cache_loc, t, p.ocl_idx64);
+    if (slot < 0 || slot >= p.num_slots) continue;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(p.kv_new + (int64_t)t * p.kv_new_stride_tok + 8 * c);
+    *reinterpret_cast<u32x4*>(pool + slot * p.kv_row_stride + 8 * c) = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // metadata build: workgroup 0 (the slot staging runs beside it)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
   if (blockIdx.x > 0) {
     stage_slots(p, blockIdx.x - 1, gridDim.x - 1);
+    save_rows(p, blockIdx.x - 1, gridDim.x - 1);
     return;
   }
   __shared__ int32_t s_req[kMaxBatch][8];

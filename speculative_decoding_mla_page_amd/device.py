@@ -20,11 +20,14 @@ class DeviceInputs:
     [sumT, H, 576]), rows / row_slots (the pool's used rows), num_slots,
     num_heads, qo_indptr, kv_indptr, kv_indices, out_cache_loc, custom_mask,
     mask_indptr, sm_scale.  Unused pool slots hold bf16 NaN when ``poison``.
+    With ``fused_save`` the draft tokens' rows are left out of the pool (their
+    slots hold the fill value) and handed over as ``kv_new`` [sumT, 576], for
+    the call to store at ``out_cache_loc`` itself.
     """
 
     def __init__(self, inst, device: str = "cuda", kv_indices_dtype: int = B.I32,
                  out_cache_loc_dtype: int = B.I64, row_stride: int = B.D_QK, poison: bool = True,
-                 q_pad_heads: int = 0, out_pad_heads: int = 0):
+                 q_pad_heads: int = 0, out_pad_heads: int = 0, fused_save: bool = False):
         self.device = torch.device(device)
         self.num_heads = int(inst.num_heads)
         self.num_slots = int(inst.num_slots)
@@ -48,6 +51,13 @@ class DeviceInputs:
         rows = torch.from_numpy(np.ascontiguousarray(inst.rows).view(np.int16)).to(d)
         slots = torch.from_numpy(np.asarray(inst.row_slots, dtype=np.int64)).to(d)
         self.pool[slots, :B.D_QK] = rows
+        self.kv_new = None
+        total_q = int(inst.qo_indptr[-1])
+        if fused_save and total_q > 0:
+            ocl = np.asarray(inst.out_cache_loc, np.int64)[:total_q]
+            new = np.ascontiguousarray(inst.pool_view()[ocl][:, :B.D_QK]).view(np.int16)
+            self.kv_new = torch.from_numpy(new).to(d)
+            self.pool[torch.from_numpy(ocl).to(d)] = fill
         idx_t = torch.int64 if kv_indices_dtype == B.I64 else torch.int32
         ocl_t = torch.int64 if out_cache_loc_dtype == B.I64 else torch.int32
         self.qo_indptr = torch.from_numpy(np.asarray(inst.qo_indptr, np.int32)).to(d)
@@ -105,7 +115,8 @@ class Verifier:
     def args(self, di: DeviceInputs, out, lse, batch_size: Optional[int] = None) -> B.Args:
         return B.make_args(di.batch if batch_size is None else batch_size, di.sm_scale, di.q,
                            di.pool, di.qo_indptr, di.kv_indptr, di.kv_indices, di.out_cache_loc,
-                           di.custom_mask, di.mask_indptr, out, lse, num_slots=di.num_slots)
+                           di.custom_mask, di.mask_indptr, out, lse, num_slots=di.num_slots,
+                           kv_new=di.kv_new)
 
     def __call__(self, di: DeviceInputs, out, lse, stream=None, batch_size: Optional[int] = None):
         B.run(self.plan, self.args(di, out, lse, batch_size), self.workspace, stream)
