@@ -162,7 +162,10 @@ mla_verify_status_t mla_verify_plan(const mla_verify_config_t* cfg, mla_verify_p
   mla_verify_layout_t& l = impl.layout;
   // every request adds at most one partly filled key range per row block
   const int64_t row_blocks_bound = (max_rows + kRowsPerItem - 1) / kRowsPerItem + c.max_batch;
-  const int64_t capacity = (int64_t)target + row_blocks_bound;
+  // room for two rounds of target items (the metadata kernel may choose
+  // shorter key ranges over two rounds when many short requests would leave
+  // one round badly balanced), plus the partly filled ranges
+  const int64_t capacity = 2 * (int64_t)target + row_blocks_bound;
   if (capacity > INT32_MAX / 2) return MLA_VERIFY_ERR_UNSUPPORTED;
   l.item_capacity = (int32_t)capacity;
   l.rows_per_item = kRowsPerItem;

@@ -82,22 +82,54 @@ __device__ void stage_slots(const KernelParams& p, int group, int groups) {
   const int total = qB + kB;
   const int per = (total + groups - 1) / groups;
   const int g0 = group * per, g1 = min(total, g0 + per);
-  for (int g = g0 + (int)threadIdx.x; g < g1; g += kMetaThreads) {
-    int lo = 0, hi = B - 1;   // last request whose keys start at or before g
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (p.kv_indptr[mid] + p.qo_indptr[mid] <= g) lo = mid; else hi = mid - 1;
+  if (g0 >= g1) return;
+  // per request, in LDS: where its keys start, its prefix start and length,
+  // its first query token and key count (0 for a request whose indptrs are
+  // out of range)
+  __shared__ int s_start[kMaxBatch], s_k0[kMaxBatch], s_P[kMaxBatch], s_q0[kMaxBatch], s_N[kMaxBatch];
+  for (int b = threadIdx.x; b < B; b += kMetaThreads) {
+    const int q0 = p.qo_indptr[b], q1 = p.qo_indptr[b + 1];
+    const int k0 = p.kv_indptr[b], k1 = p.kv_indptr[b + 1];
+    const bool ok = q0 >= 0 && q1 >= q0 && q1 <= p.max_q_tokens && k0 >= 0 && k1 >= k0 &&
+                    (int64_t)k1 <= p.max_kv_tokens;
+    s_start[b] = k0 + q0;
+    s_k0[b] = k0;
+    s_P[b] = k1 - k0;
+    s_q0[b] = q0;
+    s_N[b] = ok ? (k1 - k0) + (q1 - q0) : 0;
+  }
+  __syncthreads();
+  // kPer positions per thread at a time: every index load is issued before
+  // the first store
+  constexpr int kPer = 4;
+  for (int base = g0; base < g1; base += kPer * kMetaThreads) {
+    int64_t raw[kPer];
+    bool have[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int g = base + k * kMetaThreads + (int)threadIdx.x;
+      have[k] = false;
+      raw[k] = 0;
+      if (g >= g1) continue;
+      int lo = 0, hi = B - 1;   // last request whose keys start at or before g
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_start[mid] <= g) lo = mid; else hi = mid - 1;
+      }
+      const int j = g - s_start[lo];
+      if (j < 0 || j >= s_N[lo]) continue;
+      const int P = s_P[lo];
+      raw[k] = j < P ? load_index(p.kv_indices, (int64_t)s_k0[lo] + j, p.kv_idx64)
+                     : load_index(p.out_cache_loc, (int64_t)s_q0[lo] + (j - P), p.ocl_idx64);
+      have[k] = true;
     }
-    const int q0 = p.qo_indptr[lo], q1 = p.qo_indptr[lo + 1];
-    const int k0 = p.kv_indptr[lo], k1 = p.kv_indptr[lo + 1];
-    if (q0 < 0 || q1 < q0 || q1 > p.max_q_tokens || k0 < 0 || k1 < k0 || (int64_t)k1 > p.max_kv_tokens) continue;
-    const int j = g - (k0 + q0);
-    const int P = k1 - k0;
-    if (j < 0 || j >= P + (q1 - q0)) continue;
-    const int64_t raw = j < P ? load_index(p.kv_indices, (int64_t)k0 + j, p.kv_idx64)
-                              : load_index(p.out_cache_loc, (int64_t)q0 + (j - P), p.ocl_idx64);
-    p.slots[g] = (raw >= 0 && raw < p.num_slots) ? (int32_t)raw : -1;
-    if (p.trace) p.trace[g] = raw;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      if (!have[k]) continue;
+      const int g = base + k * kMetaThreads + (int)threadIdx.x;
+      p.slots[g] = (raw[k] >= 0 && raw[k] < p.num_slots) ? (int32_t)raw[k] : -1;
+      if (p.trace) p.trace[g] = raw[k];
+    }
   }
 }
 
@@ -136,6 +168,9 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
   __shared__ int32_t s_req[kMaxBatch][8];
   __shared__ uint32_t s_err;
   __shared__ long long s_work;
+  __shared__ int s_rowblocks;
+  __shared__ int s_scan[kMetaThreads];
+  __shared__ int s_cand_items[5];
   __shared__ int32_t s_chunk;
   __shared__ int32_t s_items;
   const int tid = threadIdx.x;
@@ -144,12 +179,16 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
   if (tid == 0) {
     s_err = 0;
     s_work = 0;
+    s_rowblocks = 0;
+    s_items = 0;
+    for (int m = 0; m < 5; ++m) s_cand_items[m] = 0;
   }
   __syncthreads();
 
   // per-request lengths and checks (prefix length = kv_indptr[b+1] - kv_indptr[b])
   uint32_t err = 0;
   long long work = 0;
+  int rowblocks = 0;
   for (int b = tid; b < B; b += kMetaThreads) {
     const int q0 = p.qo_indptr[b], q1 = p.qo_indptr[b + 1];
     const int k0 = p.kv_indptr[b], k1 = p.kv_indptr[b + 1];
@@ -169,28 +208,89 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
     s_req[b][RQ_RB] = rb;
     s_req[b][RQ_MASK0] = m0;
     work += (long long)rb * (Pc + Tc);
+    rowblocks += rb;
   }
   if (err) atomicOr(&s_err, err);
   if (work) atomicAdd(reinterpret_cast<unsigned long long*>(&s_work), (unsigned long long)work);
+  if (rowblocks) atomicAdd(&s_rowblocks, rowblocks);
   __syncthreads();
 
-  // key-range length shared by all requests: total (row block x key) work cut
-  // into about target_items pieces, rounded up to whole tiles
-  if (tid == 0) {
-    const long long per = (s_work + p.target_items - 1) / p.target_items;
-    long long chunk = ((per + kKeysPerTile - 1) / kKeysPerTile) * kKeysPerTile;
-    if (chunk < kMinChunkKeys) chunk = kMinChunkKeys;
-    if (chunk > (1LL << 30)) chunk = 1LL << 30;
-    s_chunk = (int)chunk;
-    int items = 0;
-    for (int b = 0; b < B; ++b) {
+  // key-range length shared by all requests.  Candidates cut the total (row
+  // block x key) work into about m x target_items pieces (less the row-block
+  // count, since every row block adds at most one partly filled range),
+  // rounded up to whole tiles; the one chosen has the least modelled time:
+  // rounds of target_items workgroups x (tiles per range + the per-item
+  // cost, about kItemTiles tiles), among those whose items fit the plan.
+  auto chunk_for = [&](long long slots) {
+    if (slots < 1) slots = 1;
+    const long long per_item = (s_work + slots - 1) / slots;
+    long long c = ((per_item + kKeysPerTile - 1) / kKeysPerTile) * kKeysPerTile;
+    if (c < kMinChunkKeys) c = kMinChunkKeys;
+    if (c > (1LL << 30)) c = 1LL << 30;
+    return (int)c;
+  };
+  auto items_of = [&](int b, int c) {
+    const int N = s_req[b][RQ_P] + s_req[b][RQ_T];
+    const int rb = s_req[b][RQ_RB];
+    return rb > 0 ? rb * ((N + c - 1) / c) : 0;
+  };
+  constexpr int kCands = 5;
+  constexpr long long kItemTiles = 6;
+  int cand[kCands];
+  cand[0] = chunk_for(p.target_items);
+  for (int m = 1; m < kCands; ++m) cand[m] = chunk_for((long long)m * p.target_items - s_rowblocks);
+  {
+    int mine[kCands] = {0, 0, 0, 0, 0};
+    for (int b = tid; b < B; b += kMetaThreads)
+#pragma unroll
+      for (int m = 0; m < kCands; ++m) mine[m] += items_of(b, cand[m]);
+#pragma unroll
+    for (int m = 0; m < kCands; ++m)
+      if (mine[m]) atomicAdd(&s_cand_items[m], mine[m]);   // zeroed at the start
+  }
+  __syncthreads();
+  int chunk_sel = cand[0];
+  {
+    long long best = -1;
+    for (int m = 0; m < kCands; ++m) {
+      const long long items = s_cand_items[m];
+      if (items > p.item_capacity) continue;   // none fits: cand[0], flagged below
+      const long long rounds = (items + p.target_items - 1) / p.target_items;
+      const long long cost = (rounds < 1 ? 1 : rounds) * (cand[m] / kKeysPerTile + kItemTiles);
+      if (best < 0 || cost < best) {
+        best = cost;
+        chunk_sel = cand[m];
+      }
+    }
+  }
+  // each request's first item: an exclusive scan of the item counts, each
+  // thread taking a contiguous run of requests
+  const int run = (B + kMetaThreads - 1) / kMetaThreads;
+  const int b_lo = min(B, tid * run), b_hi = min(B, b_lo + run);
+  int local = 0;
+  for (int b = b_lo; b < b_hi; ++b) local += items_of(b, chunk_sel);
+  s_scan[tid] = local;
+  __syncthreads();
+  for (int d = 1; d < kMetaThreads; d <<= 1) {
+    const int add = tid >= d ? s_scan[tid - d] : 0;
+    __syncthreads();
+    s_scan[tid] += add;
+    __syncthreads();
+  }
+  {
+    int at = s_scan[tid] - local;
+    for (int b = b_lo; b < b_hi; ++b) {
       const int N = s_req[b][RQ_P] + s_req[b][RQ_T];
       const int rb = s_req[b][RQ_RB];
-      const int chunks = rb > 0 ? (N + (int)chunk - 1) / (int)chunk : 0;
-      s_req[b][RQ_CHUNKS] = chunks;
-      s_req[b][RQ_ITEM0] = items;
-      items += rb * chunks;
+      s_req[b][RQ_CHUNKS] = rb > 0 ? (N + chunk_sel - 1) / chunk_sel : 0;
+      s_req[b][RQ_ITEM0] = at;
+      at += items_of(b, chunk_sel);
     }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int items = s_scan[kMetaThreads - 1];
+    s_chunk = chunk_sel;
     if (items > p.item_capacity) s_err |= MLA_VERIFY_DEVERR_CAPACITY;
     if (s_err & kMetaErrMask) items = 0;
     s_items = items;

@@ -64,7 +64,7 @@ def test_plan_layout_arithmetic():
     rows = lay.rows_per_item
     assert rows in (64, 128) and lay.keys_per_tile == 32 and lay.target_items == 256
     # one partly filled key range per row block, at most
-    assert lay.item_capacity == 256 + (512 * 8 + rows - 1) // rows + 8
+    assert lay.item_capacity == 2 * 256 + (512 * 8 + rows - 1) // rows + 8
     assert lay.partial_grid % 8 == 0 and lay.item_capacity <= lay.partial_grid < lay.item_capacity + 8
     assert lay.merge_grid == 512 * 8
     offs = [lay.header_offset, lay.request_offset, lay.anc_offset, lay.items_offset,

@@ -74,3 +74,15 @@ def test_bf16_rounding_ties_to_even():
     bits = gen.f32_to_bf16_bits(x)
     back = (bits.astype(np.uint32) << 16).view(np.float32)
     assert back.tolist() == [1.0, 1.0, 1.0 + 2 ** -6, -2.5, 0.0]
+
+
+def test_decode_shapes():
+    """Decode workloads: one node per request that sees itself, prefixes in range."""
+    for name, b, h in (("decode_b32_h16", 32, 16), ("decode_b64_h128", 64, 128)):
+        spec = gen.CONFIGS[name]
+        assert len(spec["prefix_lens"]) == b and spec["tree_sizes"] == [1] * b
+        assert all(512 <= p <= 8192 for p in spec["prefix_lens"]) and spec["num_heads"] == h
+    inst = gen.config("decode_b32_h16")
+    assert np.array_equal(inst.custom_mask, np.ones(32, np.uint8))
+    assert np.array_equal(np.asarray(inst.mask_indptr), np.arange(33))
+    assert np.array_equal(np.asarray(inst.qo_indptr), np.arange(33))

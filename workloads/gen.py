@@ -231,6 +231,17 @@ CONFIGS = {
 CONFIG_SEEDS = {"tiny": 1001, "p5632_t16": 1002, "p23040_t32": 1003, "p91136_t32": 1004,
                 "p91136_t32_h64": 1104}
 
+# Decode: one query token per request (T_b = 1, its own key visible), many
+# requests with prefixes drawn once, U[512, 8192], from fixed seeds.
+DECODE_PREFIXES_B32 = [int(x) for x in np.random.default_rng(3032).integers(512, 8193, size=32)]
+DECODE_PREFIXES_B64 = [int(x) for x in np.random.default_rng(3064).integers(512, 8193, size=64)]
+CONFIGS["decode_b32_h16"] = dict(prefix_lens=DECODE_PREFIXES_B32, tree_sizes=[1] * 32, num_heads=16,
+                                 num_slots=1 << 18, tree="random", outlier_frac=0.0)
+CONFIGS["decode_b64_h128"] = dict(prefix_lens=DECODE_PREFIXES_B64, tree_sizes=[1] * 64, num_heads=128,
+                                  num_slots=1 << 19, tree="random", outlier_frac=0.0)
+CONFIG_SEEDS["decode_b32_h16"] = 1201
+CONFIG_SEEDS["decode_b64_h128"] = 1202
+
 # Segmented batch: 8 requests, prefixes U[1000, 185000], trees U[8, 64].
 SEGMENTED = dict(batch=8, prefix_lo=1000, prefix_hi=185000, tree_lo=8, tree_hi=64,
                  num_heads=8, num_slots=1 << 21)
