@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MLA_VERIFY_ABI_VERSION 3
+#define MLA_VERIFY_ABI_VERSION 4
 #define MLA_VERIFY_D_QK 576          /* latent width used by Q.K^T (512 + 64 rope) */
 #define MLA_VERIFY_D_V 512           /* V = latent dims [0, 512) */
 #define MLA_VERIFY_MAX_TREE_NODES 64 /* tree visibility is packed into one 64-bit word */
@@ -66,7 +66,18 @@ enum { MLA_VERIFY_I32 = 0, MLA_VERIFY_I64 = 1 };
 enum {
   /* record every gathered slot in the workspace trace region (for bit-exact
      checks of the gather); costs one extra store per key */
-  MLA_VERIFY_FLAG_TRACE_KEYS = 1u
+  MLA_VERIFY_FLAG_TRACE_KEYS = 1u,
+  /* custom_mask holds a full row per tree node: request b's block is
+     T_b x (P_b + T_b), row-major, columns = its prefix keys then its tree
+     nodes (the layout a serving framework's tree verify passes), and
+     mask_indptr[b+1] - mask_indptr[b] = T_b * (P_b + T_b).  Only the tree
+     columns are read: the prefix stays visible to every node. */
+  MLA_VERIFY_FLAG_MASK_FULL_ROWS = 2u,
+  /* with MLA_VERIFY_FLAG_MASK_FULL_ROWS: check that every prefix column is
+     nonzero; a zero marks the keys it covers, the work items that gather them
+     write NaN rows and set MLA_VERIFY_DEVERR_MASK_PREFIX.  Costs one mask byte
+     read per (tree node, prefix key). */
+  MLA_VERIFY_FLAG_CHECK_PREFIX_MASK = 4u
 };
 
 /* bits of the device error word (first uint32 of the workspace) */
@@ -74,9 +85,11 @@ enum {
   MLA_VERIFY_DEVERR_QO_INDPTR = 1u << 0,   /* qo_indptr decreasing, negative or past max_q_tokens */
   MLA_VERIFY_DEVERR_KV_INDPTR = 1u << 1,   /* kv_indptr decreasing, negative or past max_kv_tokens */
   MLA_VERIFY_DEVERR_TREE_SIZE = 1u << 2,   /* a request has more tree nodes than max_tree_nodes */
-  MLA_VERIFY_DEVERR_MASK_INDPTR = 1u << 3, /* mask_indptr[b+1]-mask_indptr[b] != T_b*T_b, or < 0 */
+  MLA_VERIFY_DEVERR_MASK_INDPTR = 1u << 3, /* mask_indptr[b+1]-mask_indptr[b] != T_b*T_b (or
+                                              T_b*(P_b+T_b) with full rows), or < 0 */
   MLA_VERIFY_DEVERR_SLOT_RANGE = 1u << 4,  /* a kv_indices / out_cache_loc entry outside [0, num_slots) */
-  MLA_VERIFY_DEVERR_CAPACITY = 1u << 5     /* work items exceeded the plan (internal bound) */
+  MLA_VERIFY_DEVERR_CAPACITY = 1u << 5,    /* work items exceeded the plan (internal bound) */
+  MLA_VERIFY_DEVERR_MASK_PREFIX = 1u << 6  /* a prefix column of a full-row mask is zero (checked mode) */
 };
 
 /*
@@ -178,7 +191,9 @@ typedef struct {
   uint64_t partial_ml_offset; /* fp32 [item_capacity][rows_per_item][2] running max (log2 units) and sum */
   uint64_t trace_offset;      /* int64 [max_kv_tokens + max_q_tokens] gathered slots; 0 without the trace flag */
   uint64_t slots_offset;      /* int32 [max_kv_tokens + max_q_tokens] each request's keys (prefix then tree)
-                                 at kv_indptr[b] + qo_indptr[b] + j: the pool slot, -1 outside the pool */
+                                 at kv_indptr[b] + qo_indptr[b] + j: the pool slot, -1 outside the pool,
+                                 -2 for a prefix key a checked full-row mask hides */
+  uint64_t stats_offset;      /* mla_verify_compare_stats_t written by mla_verify_compare */
   int32_t item_capacity;
   int32_t rows_per_item;      /* query rows (token x head) per work item */
   int32_t keys_per_tile;      /* keys staged per inner-loop step */
@@ -217,6 +232,33 @@ mla_verify_status_t mla_verify_workspace_layout(const mla_verify_plan_t* plan,
 
 /* Static description of a status code. */
 const char* mla_verify_status_string(mla_verify_status_t status);
+
+/*
+ * Shadow comparison (the pages' "validate" mode: the serving system keeps
+ * returning its own attention result while this library's result is computed
+ * beside it and compared).  After run() on the same stream, compare() checks
+ * args->out / args->lse against the caller's reference, in the same layout,
+ * over the call's query tokens, and accumulates into the workspace's stats
+ * region (zeroed by every run()); read it after a sync.  One launch,
+ * capture-safe.  ref_lse may be NULL.  An element counts as over when
+ * |out - ref| > 2 bf16 ULP of ref (2^(floor(log2 |ref|) - 7), |ref| floored at
+ * 2^-126) or exactly one of the two is NaN.
+ */
+typedef struct {
+  uint32_t max_abs_diff_bits;  /* fp32 bits of max |out - ref| over pairs that are both finite */
+  uint32_t count_over;         /* elements over the 2-ULP bound (NaN mismatches included) */
+  uint32_t count_total;        /* elements compared */
+  uint32_t max_lse_diff_bits;  /* fp32 bits of max |lse - ref_lse| over finite pairs */
+  uint32_t count_nan_mismatch; /* out elements where exactly one of the two is NaN */
+  uint32_t count_lse_mismatch; /* lse entries where exactly one of the two is finite */
+  uint32_t reserved[2];
+} mla_verify_compare_stats_t;
+
+mla_verify_status_t mla_verify_compare(const mla_verify_plan_t* plan, const mla_verify_args_t* args,
+                                       const float* ref_out, int64_t ref_out_stride_tok,
+                                       int64_t ref_out_stride_head, const float* ref_lse,
+                                       int64_t ref_lse_stride_tok, void* workspace,
+                                       size_t workspace_bytes, void* stream);
 
 /* MLA_VERIFY_ABI_VERSION of the built library. */
 int32_t mla_verify_abi_version(void);

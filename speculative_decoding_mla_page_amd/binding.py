@@ -18,6 +18,8 @@ D_V = 512
 MAX_TREE_NODES = 64
 I32, I64 = 0, 1
 FLAG_TRACE_KEYS = 1
+FLAG_MASK_FULL_ROWS = 2
+FLAG_CHECK_PREFIX_MASK = 4
 
 OK = 0
 ERR_INVALID_ARGUMENT = 1
@@ -32,6 +34,7 @@ DEVERR_TREE_SIZE = 1 << 2
 DEVERR_MASK_INDPTR = 1 << 3
 DEVERR_SLOT_RANGE = 1 << 4
 DEVERR_CAPACITY = 1 << 5
+DEVERR_MASK_PREFIX = 1 << 6
 
 PHASE_META, PHASE_PARTIAL, PHASE_MERGE = 0, 1, 2
 
@@ -93,6 +96,7 @@ class Layout(ctypes.Structure):
         ("partial_ml_offset", ctypes.c_uint64),
         ("trace_offset", ctypes.c_uint64),
         ("slots_offset", ctypes.c_uint64),
+        ("stats_offset", ctypes.c_uint64),
         ("item_capacity", ctypes.c_int32),
         ("rows_per_item", ctypes.c_int32),
         ("keys_per_tile", ctypes.c_int32),
@@ -101,6 +105,18 @@ class Layout(ctypes.Structure):
         ("merge_grid", ctypes.c_int32),
         ("meta_grid", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
+    ]
+
+
+class CompareStats(ctypes.Structure):
+    _fields_ = [
+        ("max_abs_diff_bits", ctypes.c_uint32),
+        ("count_over", ctypes.c_uint32),
+        ("count_total", ctypes.c_uint32),
+        ("max_lse_diff_bits", ctypes.c_uint32),
+        ("count_nan_mismatch", ctypes.c_uint32),
+        ("count_lse_mismatch", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32 * 2),
     ]
 
 
@@ -134,6 +150,10 @@ def lib() -> ctypes.CDLL:
                                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                            ctypes.c_int32]
         l.mla_verify_run_phase.restype = ctypes.c_int
+        l.mla_verify_compare.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args), ctypes.c_void_p,
+                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        l.mla_verify_compare.restype = ctypes.c_int
         l.mla_verify_status_string.argtypes = [ctypes.c_int]
         l.mla_verify_status_string.restype = ctypes.c_char_p
         l.mla_verify_abi_version.argtypes = []
@@ -220,6 +240,17 @@ def make_args(batch_size: int, sm_scale: float, q, kv_pool, qo_indptr, kv_indptr
     a.kv_new = _ptr(kv_new)
     a.kv_new_stride_tok = kv_new.stride(0) if kv_new is not None else 0
     return a
+
+
+def compare(p: Plan, args: Args, ref_out, ref_lse, workspace, stream=None) -> None:
+    """Enqueue the shadow comparison of args.out / args.lse against a reference
+    (torch tensors in the same layout) into the workspace's stats region."""
+    st = lib().mla_verify_compare(ctypes.byref(p), ctypes.byref(args), _ptr(ref_out), ref_out.stride(0),
+                                  ref_out.stride(1), _ptr(ref_lse),
+                                  ref_lse.stride(0) if ref_lse is not None else 0, _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != OK:
+        raise MlaVerifyError(st, "mla_verify_compare")
 
 
 def _stream(stream) -> int:

@@ -102,6 +102,7 @@ KernelParams make_params(const PlanImpl& pl, const mla_verify_args_t* a, void* w
   p.part_o = reinterpret_cast<float*>(base + l.partial_o_offset);
   p.part_ml = reinterpret_cast<float*>(base + l.partial_ml_offset);
   p.slots = reinterpret_cast<int32_t*>(base + l.slots_offset);
+  p.stats = reinterpret_cast<mla_verify_compare_stats_t*>(base + l.stats_offset);
   p.trace = (c.flags & MLA_VERIFY_FLAG_TRACE_KEYS) ? reinterpret_cast<int64_t*>(base + l.trace_offset)
                                                    : nullptr;
   return p;
@@ -134,7 +135,12 @@ mla_verify_status_t mla_verify_plan(const mla_verify_config_t* cfg, mla_verify_p
   if ((c.kv_indices_dtype != MLA_VERIFY_I32 && c.kv_indices_dtype != MLA_VERIFY_I64) ||
       (c.out_cache_loc_dtype != MLA_VERIFY_I32 && c.out_cache_loc_dtype != MLA_VERIFY_I64))
     return MLA_VERIFY_ERR_INVALID_ARGUMENT;
-  if (c.flags & ~(uint32_t)MLA_VERIFY_FLAG_TRACE_KEYS) return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  if (c.flags & ~(uint32_t)(MLA_VERIFY_FLAG_TRACE_KEYS | MLA_VERIFY_FLAG_MASK_FULL_ROWS |
+                            MLA_VERIFY_FLAG_CHECK_PREFIX_MASK))
+    return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  // the prefix check reads the prefix columns of full mask rows
+  if ((c.flags & MLA_VERIFY_FLAG_CHECK_PREFIX_MASK) && !(c.flags & MLA_VERIFY_FLAG_MASK_FULL_ROWS))
+    return MLA_VERIFY_ERR_INVALID_ARGUMENT;
   for (int i = 0; i < 7; ++i)
     if (c.reserved[i]) return MLA_VERIFY_ERR_INVALID_ARGUMENT;
   if (c.max_tree_nodes > MLA_VERIFY_MAX_TREE_NODES || c.max_batch > kMaxBatch)
@@ -201,6 +207,8 @@ mla_verify_status_t mla_verify_plan(const mla_verify_config_t* cfg, mla_verify_p
   }
   l.slots_offset = off;
   off = align_up(off + ((uint64_t)c.max_kv_tokens + c.max_q_tokens) * sizeof(int32_t));
+  l.stats_offset = off;
+  off = align_up(off + sizeof(mla_verify_compare_stats_t));
   l.total_bytes = off;
 
   memset(plan, 0, sizeof(*plan));
@@ -239,6 +247,30 @@ mla_verify_status_t mla_verify_run_phase(const mla_verify_plan_t* plan, const ml
   else if (phase == 1) rc = launch_partial(p, pl->layout, stream);
   else rc = launch_merge(p, pl->layout, stream);
   return rc == 0 ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;
+}
+
+mla_verify_status_t mla_verify_compare(const mla_verify_plan_t* plan, const mla_verify_args_t* args,
+                                       const float* ref_out, int64_t ref_out_stride_tok,
+                                       int64_t ref_out_stride_head, const float* ref_lse,
+                                       int64_t ref_lse_stride_tok, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  const PlanImpl* pl = as_impl(plan);
+  if (!pl) return MLA_VERIFY_ERR_BAD_PLAN;
+  const mla_verify_status_t st = check_args(*pl, args, workspace, workspace_bytes);
+  if (st != MLA_VERIFY_OK) return st;
+  // the reference is read like out: 16-byte rows
+  if (!ref_out || !aligned(ref_out, 16) || ref_out_stride_tok <= 0 || ref_out_stride_head <= 0 ||
+      ref_out_stride_tok % 4 || ref_out_stride_head % 4)
+    return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  if (ref_lse && (!args->lse || !aligned(ref_lse, 4) || ref_lse_stride_tok <= 0))
+    return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  KernelParams p = make_params(*pl, args, workspace);
+  p.ref_out = ref_out;
+  p.ref_out_stride_tok = ref_out_stride_tok;
+  p.ref_out_stride_head = ref_out_stride_head;
+  p.ref_lse = ref_lse;
+  p.ref_lse_stride_tok = ref_lse_stride_tok;
+  return launch_compare(p, pl->layout, stream) == 0 ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;
 }
 
 mla_verify_status_t mla_verify_run(const mla_verify_plan_t* plan, const mla_verify_args_t* args,

@@ -43,6 +43,7 @@ struct WsHeader {
 constexpr uint32_t kMetaErrMask = MLA_VERIFY_DEVERR_QO_INDPTR | MLA_VERIFY_DEVERR_KV_INDPTR |
                                   MLA_VERIFY_DEVERR_TREE_SIZE | MLA_VERIFY_DEVERR_MASK_INDPTR |
                                   MLA_VERIFY_DEVERR_CAPACITY;
+constexpr int32_t kSlotMaskedPrefix = -2;   // staged slot of a prefix key a checked full-row mask hides
 
 struct PlanImpl {
   uint32_t magic;
@@ -95,10 +96,18 @@ struct KernelParams {
   float* part_ml;
   int64_t* trace;
   int32_t* slots;
+  mla_verify_compare_stats_t* stats;
+  // shadow comparison only
+  const float* ref_out;
+  int64_t ref_out_stride_tok;
+  int64_t ref_out_stride_head;
+  const float* ref_lse;
+  int64_t ref_lse_stride_tok;
 };
 
 int launch_meta(const KernelParams& p, const mla_verify_layout_t& lay, void* stream);
 int launch_partial(const KernelParams& p, const mla_verify_layout_t& lay, void* stream);
 int launch_merge(const KernelParams& p, const mla_verify_layout_t& lay, void* stream);
+int launch_compare(const KernelParams& p, const mla_verify_layout_t& lay, void* stream);
 
 }  // namespace mlav

@@ -87,6 +87,8 @@ __device__ void stage_slots(const KernelParams& p, int group, int groups) {
   // its first query token and key count (0 for a request whose indptrs are
   // out of range)
   __shared__ int s_start[kMaxBatch], s_k0[kMaxBatch], s_P[kMaxBatch], s_q0[kMaxBatch], s_N[kMaxBatch];
+  __shared__ int s_m0[kMaxBatch];   // full-row mask block of the request, -1 when not checked
+  const bool check_prefix = (p.flags & MLA_VERIFY_FLAG_CHECK_PREFIX_MASK) != 0;
   for (int b = threadIdx.x; b < B; b += kMetaThreads) {
     const int q0 = p.qo_indptr[b], q1 = p.qo_indptr[b + 1];
     const int k0 = p.kv_indptr[b], k1 = p.kv_indptr[b + 1];
@@ -97,6 +99,11 @@ __device__ void stage_slots(const KernelParams& p, int group, int groups) {
     s_P[b] = k1 - k0;
     s_q0[b] = q0;
     s_N[b] = ok ? (k1 - k0) + (q1 - q0) : 0;
+    // the prefix columns are read only where the block has its full size
+    const int m0 = check_prefix ? p.mask_indptr[b] : -1;
+    const int m1 = check_prefix ? p.mask_indptr[b + 1] : -1;
+    const long long full = (long long)(q1 - q0) * ((long long)(k1 - k0) + (q1 - q0));
+    s_m0[b] = (check_prefix && ok && m0 >= 0 && (long long)m1 - m0 == full) ? m0 : -1;
   }
   __syncthreads();
   // kPer positions per thread at a time: every index load is issued before
@@ -104,11 +111,12 @@ __device__ void stage_slots(const KernelParams& p, int group, int groups) {
   constexpr int kPer = 4;
   for (int base = g0; base < g1; base += kPer * kMetaThreads) {
     int64_t raw[kPer];
-    bool have[kPer];
+    bool have[kPer], hidden[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       const int g = base + k * kMetaThreads + (int)threadIdx.x;
       have[k] = false;
+      hidden[k] = false;
       raw[k] = 0;
       if (g >= g1) continue;
       int lo = 0, hi = B - 1;   // last request whose keys start at or before g
@@ -122,12 +130,18 @@ __device__ void stage_slots(const KernelParams& p, int group, int groups) {
       raw[k] = j < P ? load_index(p.kv_indices, (int64_t)s_k0[lo] + j, p.kv_idx64)
                      : load_index(p.out_cache_loc, (int64_t)s_q0[lo] + (j - P), p.ocl_idx64);
       have[k] = true;
+      if (j < P && s_m0[lo] >= 0) {
+        // column j of every node's full mask row must be nonzero
+        const int T = s_N[lo] - P;
+        const uint8_t* col = p.custom_mask + s_m0[lo] + j;
+        for (int i = 0; i < T; ++i) hidden[k] |= col[(size_t)i * (P + T)] == 0;
+      }
     }
 #pragma unroll
     for (int k = 0; k < kPer; ++k) {
       if (!have[k]) continue;
       const int g = base + k * kMetaThreads + (int)threadIdx.x;
-      p.slots[g] = (raw[k] >= 0 && raw[k] < p.num_slots) ? (int32_t)raw[k] : -1;
+      p.slots[g] = hidden[k] ? kSlotMaskedPrefix : (raw[k] >= 0 && raw[k] < p.num_slots) ? (int32_t)raw[k] : -1;
       if (p.trace) p.trace[g] = raw[k];
     }
   }
@@ -186,6 +200,8 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
   __syncthreads();
 
   // per-request lengths and checks (prefix length = kv_indptr[b+1] - kv_indptr[b])
+  const bool full_rows = (p.flags & MLA_VERIFY_FLAG_MASK_FULL_ROWS) != 0;
+  if (tid < (int)(sizeof(mla_verify_compare_stats_t) / 4)) reinterpret_cast<uint32_t*>(p.stats)[tid] = 0;
   uint32_t err = 0;
   long long work = 0;
   int rowblocks = 0;
@@ -197,7 +213,8 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
     if (q0 < 0 || T < 0 || q1 > p.max_q_tokens || (b == 0 && q0 != 0)) err |= MLA_VERIFY_DEVERR_QO_INDPTR;
     if (k0 < 0 || P < 0 || (long long)k1 > p.max_kv_tokens) err |= MLA_VERIFY_DEVERR_KV_INDPTR;
     if (T > p.max_tree_nodes) err |= MLA_VERIFY_DEVERR_TREE_SIZE;
-    if (m0 < 0 || (long long)(m1 - m0) != (long long)T * T) err |= MLA_VERIFY_DEVERR_MASK_INDPTR;
+    const long long mask_size = full_rows ? (long long)T * ((long long)T + P) : (long long)T * T;
+    if (m0 < 0 || (long long)(m1 - m0) != mask_size) err |= MLA_VERIFY_DEVERR_MASK_INDPTR;
     const int Tc = T < 0 ? 0 : T, Pc = P < 0 ? 0 : P;
     const int rows = Tc * H;
     const int rb = (rows + kRowsPerItem - 1) / kRowsPerItem;
@@ -341,7 +358,9 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
     const int b = lo;
     const int T = s_req[b][RQ_T];
     const int i = t - s_req[b][RQ_Q0];
-    const uint8_t* row = p.custom_mask + s_req[b][RQ_MASK0] + (size_t)i * T;
+    // T x T blocks, or full rows of P + T columns whose tree part starts at P
+    const int Pm = full_rows ? s_req[b][RQ_P] : 0;
+    const uint8_t* row = p.custom_mask + s_req[b][RQ_MASK0] + (size_t)i * (Pm + T) + Pm;
     uint64_t w = 0;
     for (int k = 0; k < T; ++k) w |= (uint64_t)(row[k] != 0) << k;
     p.anc[t] = w;
@@ -469,9 +488,10 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
   // ---- slots: blocks of kIdxKeys keys staged in LDS (double buffered) ----
   // The score waves copy the int32 slots of block b straight into LDS, lane
   // = key, with the tile loads.  Keys past the range end re-read the range's
-  // last slot.  A slot of -1 (outside the pool) reads slot 0 instead and
-  // poisons the item: its rows become NaN.
-  bool poison = false;
+  // last slot.  A slot of -1 (outside the pool) or -2 (a prefix key that a
+  // checked full-row mask hides) reads slot 0 instead and poisons the item:
+  // its rows become NaN.
+  bool out_of_pool = false, hidden = false;
   auto issue_idx = [&](int blk) {
     const int j = min(key0 + blk * kIdxKeys + 64 * wave + lane, key1 - 1);
     dma4(kslots + j, lds_addr(&s_idx[blk & 1][64 * wave]));
@@ -502,14 +522,13 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
       // the V keys' slots in one 16-byte broadcast read (4r is 4-aligned
       // in the block)
       const i32x4 v4 = *reinterpret_cast<const i32x4*>(idx + jt + 4 * r);
-      int32_t any_bad = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int32_t v = __builtin_amdgcn_readfirstlane(v4[i]);
-        any_bad |= v;
+        hidden |= v == kSlotMaskedPrefix;
+        out_of_pool |= v < 0 && v != kSlotMaskedPrefix;
         ts.v[i] = max(v, 0);
       }
-      poison |= any_bad < 0;
       ts.rope = 0;
     }
     return ts;
@@ -706,8 +725,12 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
       if (lane == 0) reinterpret_cast<uint8_t*>(&s_rescale[i & 1])[r] = any_need;
       __builtin_amdgcn_s_setprio(0);
     }
-    poison = __syncthreads_or(poison);
-    if (poison && tid == 0) atomicOr(&p.hdr->err, (uint32_t)MLA_VERIFY_DEVERR_SLOT_RANGE);
+    out_of_pool = __syncthreads_or(out_of_pool);
+    hidden = __syncthreads_or(hidden);
+    const bool poison = out_of_pool || hidden;
+    if (tid == 0 && poison)
+      atomicOr(&p.hdr->err, (out_of_pool ? (uint32_t)MLA_VERIFY_DEVERR_SLOT_RANGE : 0u) |
+                                (hidden ? (uint32_t)MLA_VERIFY_DEVERR_MASK_PREFIX : 0u));
     if (row_ok && g == 0) {
       float* pm = p.part_ml + ((size_t)item * kRowsPerItem + r_local) * 2;
       pm[0] = m_run;
@@ -816,7 +839,8 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
       pv_iteration(i, std::integral_constant<int, 0>{});
       if (i + 1 <= ntiles + 1) pv_iteration(i + 1, std::integral_constant<int, 1>{});
     }
-    poison = __syncthreads_or(poison);
+    out_of_pool = __syncthreads_or(out_of_pool);
+    hidden = __syncthreads_or(hidden);
 #pragma unroll
     for (int rt = 0; rt < kWaves; ++rt) {
       const int rl = 16 * rt + n;
@@ -938,6 +962,76 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(KernelParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// shadow comparison: one workgroup of 128 threads per query row (token,
+// head), 4 output elements per thread, against the caller's reference.
+// Per-row partial statistics are combined in LDS, then added into the
+// workspace stats (zeroed by the metadata launch) with global atomics; the
+// maxima are non-negative floats, compared as their bit patterns.
+// ---------------------------------------------------------------------------
+constexpr int kCompareThreads = 128;
+__device__ __forceinline__ float bf16_ulp_at(float r) {
+  // 2^(floor(log2 |r|) - 7) with |r| floored at 2^-126
+  const uint32_t e = (__float_as_uint(r) >> 23) & 0xffu;   // biased exponent
+  const uint32_t ee = e < 1u ? 1u : e;                      // zero and subnormals: as 2^-126
+  // 2^(ee - 134): normal for ee >= 8, else the subnormal with that one bit set
+  return __uint_as_float(ee >= 8u ? (ee - 7u) << 23 : 1u << (15u + ee));
+}
+__global__ __launch_bounds__(kCompareThreads) void compare_kernel(KernelParams p) {
+  __shared__ uint32_t s_max, s_over, s_nan;
+  const int H = p.num_heads;
+  const int row = blockIdx.x;
+  const int t = row / H, h = row % H;
+  if (t >= p.hdr->total_q) return;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    s_max = 0;
+    s_over = 0;
+    s_nan = 0;
+  }
+  __syncthreads();
+  const f32x4 o = *reinterpret_cast<const f32x4*>(p.out + (int64_t)t * p.out_stride_tok +
+                                                  (int64_t)h * p.out_stride_head + 4 * tid);
+  const f32x4 r = *reinterpret_cast<const f32x4*>(p.ref_out + (int64_t)t * p.ref_out_stride_tok +
+                                                  (int64_t)h * p.ref_out_stride_head + 4 * tid);
+  uint32_t mx = 0, over = 0, nan = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const bool on = isnan(o[k]), rn = isnan(r[k]);
+    if (on != rn) {
+      ++nan;
+      ++over;
+    } else if (!on) {
+      const float d = fabsf(o[k] - r[k]);
+      if (isfinite(d)) mx = max(mx, __float_as_uint(d));
+      if (!(d <= 2.f * bf16_ulp_at(r[k])) && o[k] != r[k]) ++over;
+    }
+  }
+  atomicMax(&s_max, mx);
+  if (over) atomicAdd(&s_over, over);
+  if (nan) atomicAdd(&s_nan, nan);
+  __syncthreads();
+  if (tid == 0) {
+    mla_verify_compare_stats_t* st = p.stats;
+    atomicMax(&st->max_abs_diff_bits, s_max);
+    if (s_over) atomicAdd(&st->count_over, s_over);
+    if (s_nan) atomicAdd(&st->count_nan_mismatch, s_nan);
+    atomicAdd(&st->count_total, (uint32_t)kDv);
+    if (p.ref_lse && p.lse) {
+      const float a = p.lse[(int64_t)t * p.lse_stride_tok + h];
+      const float b = p.ref_lse[(int64_t)t * p.ref_lse_stride_tok + h];
+      if (isfinite(a) && isfinite(b)) atomicMax(&st->max_lse_diff_bits, __float_as_uint(fabsf(a - b)));
+      else if (isfinite(a) != isfinite(b) || isnan(a) != isnan(b)) atomicAdd(&st->count_lse_mismatch, 1u);
+    }
+  }
+}
+
+int launch_compare(const KernelParams& p, const mla_verify_layout_t& lay, void* stream) {
+  if (lay.merge_grid <= 0) return 0;
+  hipLaunchKernelGGL(compare_kernel, dim3(lay.merge_grid), dim3(kCompareThreads), 0, (hipStream_t)stream, p);
+  return (int)hipGetLastError();
+}
+
 int launch_meta(const KernelParams& p, const mla_verify_layout_t& lay, void* stream) {
   hipLaunchKernelGGL(meta_kernel, dim3(lay.meta_grid), dim3(kMetaThreads), 0, (hipStream_t)stream, p);
   return (int)hipGetLastError();

@@ -24,14 +24,15 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert {"mla_verify_plan", "mla_verify_workspace_size", "mla_verify_run"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.mla_verify_abi_version() == 3
+    assert lib.mla_verify_abi_version() == 4
 
 
 def test_struct_layout_matches_header(tmp_path):
     """Compile a probe of the header with gcc and compare sizes/offsets with the ctypes mirror."""
     probe = tmp_path / "probe.c"
     fields = {"mla_verify_config_t": B.Config, "mla_verify_args_t": B.Args,
-              "mla_verify_layout_t": B.Layout, "mla_verify_plan_t": B.Plan}
+              "mla_verify_layout_t": B.Layout, "mla_verify_plan_t": B.Plan,
+              "mla_verify_compare_stats_t": B.CompareStats}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "mla_verify.h"', 'int main(void){']
     for cname, py in fields.items():
         lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
@@ -101,6 +102,7 @@ def test_plan_is_a_plain_value():
     (dict(max_batch=4096), B.ERR_UNSUPPORTED),
     (dict(kv_indices_dtype=7), B.ERR_INVALID_ARGUMENT),
     (dict(flags=0x80), B.ERR_INVALID_ARGUMENT),
+    (dict(flags=B.FLAG_CHECK_PREFIX_MASK), B.ERR_INVALID_ARGUMENT),   # needs full mask rows
     (dict(max_kv_tokens=-1), B.ERR_INVALID_ARGUMENT),
     (dict(max_kv_tokens=2 ** 31), B.ERR_UNSUPPORTED),
 ])
@@ -180,3 +182,10 @@ def test_run_rejects_small_or_misaligned_workspace():
 def test_status_strings():
     assert B.status_string(B.OK) == "ok"
     assert "workspace" in B.status_string(B.ERR_WORKSPACE_TOO_SMALL)
+
+
+def test_mask_layout_flags_plan():
+    """Full-row masks and the prefix check are plan options; the stats region follows the slots."""
+    lay = B.layout(_plan(flags=B.FLAG_MASK_FULL_ROWS | B.FLAG_CHECK_PREFIX_MASK))
+    assert lay.stats_offset % 256 == 0 and lay.stats_offset >= lay.slots_offset + (1_480_000 + 512) * 4
+    assert lay.total_bytes >= lay.stats_offset + ctypes.sizeof(B.CompareStats)
