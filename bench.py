@@ -126,6 +126,8 @@ def main():
                     help="extra calls each preceded by a 1 GiB cache scrub (reported, not the value)")
     ap.add_argument("--fused-save-calls", type=int, default=50,
                     help="extra calls that also store the draft rows into the pool (reported, not the value)")
+    ap.add_argument("--compact-calls", type=int, default=5,
+                    help="prefix compactions onto fresh slots, then the call again (reported, not the value)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (a known-size "
                          "kernel for scaling hardware byte counters)")
@@ -239,6 +241,41 @@ def main():
                  "meta_us": float(np.median([e[0].elapsed_time(e[1]) for e in fe]) * 1e3),
                  "rows_saved": int(di.total_q), "calls": args.fused_save_calls}
 
+    # prefix compaction (KV defragmentation) onto fresh contiguous slots, then
+    # the same call on the compacted pool; last, since it rewrites the inputs
+    compaction = None
+    if args.compact_calls > 0:
+        if ver.error_word() != 0:
+            raise RuntimeError(f"device error word {ver.error_word():#x}")
+        base = di.num_slots
+        di.pool = torch.cat([di.pool, torch.empty((di.total_kv, di.pool.shape[1]), dtype=di.pool.dtype,
+                                                  device=di.pool.device)])
+        di.num_slots = di.pool.shape[0]
+        a = ver.args(di, out, lse)
+        dst = torch.tensor([base + int(x) for x in np.asarray(inst.kv_indptr)[:-1]], dtype=torch.int64,
+                           device=di.pool.device)
+        err = torch.zeros(1, dtype=torch.int32, device=di.pool.device)
+        ce2 = [torch.cuda.Event(enable_timing=True) for _ in range(args.compact_calls + 1)]
+        ce2[0].record(stream)
+        for k in range(args.compact_calls):
+            B.compact(ver.plan, a, dst, err, sp)   # the first call moves, the rest copy in place
+            ce2[k + 1].record(stream)
+        for _ in range(5):
+            B.run(ver.plan, a, ver.workspace, sp)
+        ve = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ve[0].record(stream)
+        for _ in range(args.steps):
+            B.run(ver.plan, a, ver.workspace, sp)
+        ve[1].record(stream)
+        torch.cuda.synchronize()
+        if int(err.item()) != 0 or ver.error_word() != 0:
+            raise RuntimeError("compaction reported an error")
+        compaction = {"first_call_us": ce2[0].elapsed_time(ce2[1]) * 1e3,
+                      "us_per_call": float(np.median([ce2[k].elapsed_time(ce2[k + 1])
+                                                      for k in range(args.compact_calls)]) * 1e3),
+                      "rows": int(di.total_kv), "bytes_moved": int(di.total_kv) * 1152 * 2,
+                      "verify_us_per_call_after": ve[0].elapsed_time(ve[1]) * 1e3 / args.steps}
+
     # reference numbers: the same call checked for the device error word
     if ver.error_word() != 0:
         raise RuntimeError(f"device error word {ver.error_word():#x}")
@@ -289,6 +326,7 @@ def main():
         "roofline_call": {"t_roof_us": max(t_hbm, t_mfma) * 1e6, "frac": max(t_hbm, t_mfma) / (us_call * 1e-6),
                           "frac_hbm": t_hbm / (us_call * 1e-6), "frac_mfma": t_mfma / (us_call * 1e-6)},
         "fused_kv_save": fused,
+        "compaction": compaction,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MLA_VERIFY_ABI_VERSION 4
+#define MLA_VERIFY_ABI_VERSION 5
 #define MLA_VERIFY_D_QK 576          /* latent width used by Q.K^T (512 + 64 rope) */
 #define MLA_VERIFY_D_V 512           /* V = latent dims [0, 512) */
 #define MLA_VERIFY_MAX_TREE_NODES 64 /* tree visibility is packed into one 64-bit word */
@@ -259,6 +259,25 @@ mla_verify_status_t mla_verify_compare(const mla_verify_plan_t* plan, const mla_
                                        int64_t ref_out_stride_head, const float* ref_lse,
                                        int64_t ref_lse_stride_tok, void* workspace,
                                        size_t workspace_bytes, void* stream);
+
+/*
+ * Prefix compaction (KV defragmentation): request b's prefix rows (the slots
+ * kv_indices[kv_indptr[b] + j], j < P_b) are copied to the contiguous slots
+ * dst_start[b] + j, and those kv_indices entries are rewritten to the new
+ * slots, in place.  Uses batch_size, kv_pool (writable), kv_row_stride,
+ * num_slots, kv_indptr and kv_indices (writable, the plan's dtype) of args.
+ *   dst_start    int64 [batch_size], device memory.
+ *   error_word   int32, device memory, zeroed by the caller: a row whose old
+ *                or new slot lies outside the pool, or a request whose indptrs
+ *                are out of range, is left as it is and sets
+ *                MLA_VERIFY_DEVERR_SLOT_RANGE / _KV_INDPTR here.
+ * The destination slots must hold no row that any request still reads (they
+ * are fresh slots from the caller's allocator); the old slots may be freed
+ * once the call has run.  One launch whose grid depends on the plan only,
+ * capture-safe; no workspace.
+ */
+mla_verify_status_t mla_verify_compact(const mla_verify_plan_t* plan, const mla_verify_args_t* args,
+                                       const int64_t* dst_start, int32_t* error_word, void* stream);
 
 /* MLA_VERIFY_ABI_VERSION of the built library. */
 int32_t mla_verify_abi_version(void);

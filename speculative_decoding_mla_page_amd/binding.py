@@ -154,6 +154,9 @@ def lib() -> ctypes.CDLL:
                                          ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
                                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         l.mla_verify_compare.restype = ctypes.c_int
+        l.mla_verify_compact.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args), ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+        l.mla_verify_compact.restype = ctypes.c_int
         l.mla_verify_status_string.argtypes = [ctypes.c_int]
         l.mla_verify_status_string.restype = ctypes.c_char_p
         l.mla_verify_abi_version.argtypes = []
@@ -251,6 +254,17 @@ def compare(p: Plan, args: Args, ref_out, ref_lse, workspace, stream=None) -> No
                                   workspace.numel() * workspace.element_size(), _stream(stream))
     if st != OK:
         raise MlaVerifyError(st, "mla_verify_compare")
+
+
+def compact(p: Plan, args: Args, dst_start, error_word, stream=None) -> None:
+    """Enqueue the prefix compaction: each request's prefix rows move to the
+    contiguous slots starting at dst_start[b] (int64 device tensor) and
+    kv_indices is rewritten in place; problems are ORed into error_word
+    (int32 device tensor, zeroed by the caller)."""
+    st = lib().mla_verify_compact(ctypes.byref(p), ctypes.byref(args), _ptr(dst_start), _ptr(error_word),
+                                  _stream(stream))
+    if st != OK:
+        raise MlaVerifyError(st, "mla_verify_compact")
 
 
 def _stream(stream) -> int:

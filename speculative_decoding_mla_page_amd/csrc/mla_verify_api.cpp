@@ -273,6 +273,32 @@ mla_verify_status_t mla_verify_compare(const mla_verify_plan_t* plan, const mla_
   return launch_compare(p, pl->layout, stream) == 0 ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;
 }
 
+mla_verify_status_t mla_verify_compact(const mla_verify_plan_t* plan, const mla_verify_args_t* args,
+                                       const int64_t* dst_start, int32_t* error_word, void* stream) {
+  const PlanImpl* pl = as_impl(plan);
+  if (!pl) return MLA_VERIFY_ERR_BAD_PLAN;
+  if (!args || !dst_start || !error_word || !aligned(dst_start, 8) || !aligned(error_word, 4))
+    return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  const mla_verify_config_t& c = pl->cfg;
+  if (args->batch_size < 0 || args->batch_size > c.max_batch || !args->kv_pool || !args->kv_indptr ||
+      !args->kv_indices || !aligned(args->kv_pool, 16) || args->kv_row_stride < kDqk ||
+      args->kv_row_stride % 8 || args->num_slots <= 0 || !aligned(args->kv_indptr, 4) ||
+      !aligned(args->kv_indices, c.kv_indices_dtype == MLA_VERIFY_I64 ? 8 : 4))
+    return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  if (args->num_slots > INT32_MAX || args->kv_row_stride > (INT32_MAX >> 1)) return MLA_VERIFY_ERR_UNSUPPORTED;
+  KernelParams p;
+  memset(&p, 0, sizeof(p));
+  p.batch = args->batch_size;
+  p.kv_pool = reinterpret_cast<const uint16_t*>(args->kv_pool);
+  p.kv_row_stride = args->kv_row_stride;
+  p.num_slots = args->num_slots;
+  p.kv_indptr = args->kv_indptr;
+  p.kv_indices = args->kv_indices;
+  p.kv_idx64 = c.kv_indices_dtype == MLA_VERIFY_I64;
+  p.max_kv_tokens = c.max_kv_tokens;
+  return launch_compact(p, dst_start, error_word, stream) == 0 ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;
+}
+
 mla_verify_status_t mla_verify_run(const mla_verify_plan_t* plan, const mla_verify_args_t* args,
                                    void* workspace, size_t workspace_bytes, void* stream) {
   const PlanImpl* pl = as_impl(plan);

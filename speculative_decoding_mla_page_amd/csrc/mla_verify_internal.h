@@ -109,5 +109,6 @@ int launch_meta(const KernelParams& p, const mla_verify_layout_t& lay, void* str
 int launch_partial(const KernelParams& p, const mla_verify_layout_t& lay, void* stream);
 int launch_merge(const KernelParams& p, const mla_verify_layout_t& lay, void* stream);
 int launch_compare(const KernelParams& p, const mla_verify_layout_t& lay, void* stream);
+int launch_compact(const KernelParams& p, const int64_t* dst_start, int32_t* error_word, void* stream);
 
 }  // namespace mlav

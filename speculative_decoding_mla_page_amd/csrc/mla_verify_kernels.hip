@@ -1032,6 +1032,70 @@ int launch_compare(const KernelParams& p, const mla_verify_layout_t& lay, void* 
   return (int)hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// prefix compaction: one wave per prefix row (grid-stride over all rows of
+// the batch).  The wave reads the row's old slot, copies its 72 16-byte units
+// (lanes 0-63, then lanes 0-7 again), then lane 0 rewrites the index, so every
+// read of the old index precedes its rewrite.
+// ---------------------------------------------------------------------------
+constexpr int kCompactThreads = 256;
+constexpr int kCompactGroups = 1024;
+__global__ __launch_bounds__(kCompactThreads) void compact_kernel(KernelParams p, const int64_t* dst_start,
+                                                                  int32_t* error_word) {
+  __shared__ int s_k0[kMaxBatch + 1];
+  const int B = p.batch;
+  if (B <= 0) return;
+  const int kB = p.kv_indptr[B];
+  if (kB < 0 || (int64_t)kB > p.max_kv_tokens) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(error_word, (int32_t)MLA_VERIFY_DEVERR_KV_INDPTR);
+    return;
+  }
+  for (int b = threadIdx.x; b <= B; b += kCompactThreads) s_k0[b] = p.kv_indptr[b];
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int waves = gridDim.x * (kCompactThreads / 64);
+  uint16_t* pool = const_cast<uint16_t*>(p.kv_pool);
+  for (int g = blockIdx.x * (kCompactThreads / 64) + (int)(threadIdx.x >> 6); g < kB; g += waves) {
+    int lo = 0, hi = B - 1;   // last request whose prefix starts at or before g
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_k0[mid] <= g) lo = mid; else hi = mid - 1;
+    }
+    const int k0 = s_k0[lo], k1 = s_k0[lo + 1];
+    if (k0 < 0 || k1 < k0 || g >= k1) {
+      if (lane == 0) atomicOr(error_word, (int32_t)MLA_VERIFY_DEVERR_KV_INDPTR);
+      continue;
+    }
+    const int64_t src = load_index(p.kv_indices, g, p.kv_idx64);
+    const int64_t dst = dst_start[lo] + (g - k0);
+    if (src < 0 || src >= p.num_slots || dst < 0 || dst >= p.num_slots) {
+      if (lane == 0) atomicOr(error_word, (int32_t)MLA_VERIFY_DEVERR_SLOT_RANGE);
+      continue;
+    }
+    const uint16_t* from = pool + src * p.kv_row_stride;
+    uint16_t* to = pool + dst * p.kv_row_stride;
+    const u32x4 a = *reinterpret_cast<const u32x4*>(from + 8 * lane);
+    u32x4 b2 = u32x4{0u, 0u, 0u, 0u};
+    if (lane < kRowUnits - 64) b2 = *reinterpret_cast<const u32x4*>(from + 8 * (64 + lane));
+    *reinterpret_cast<u32x4*>(to + 8 * lane) = a;
+    if (lane < kRowUnits - 64) *reinterpret_cast<u32x4*>(to + 8 * (64 + lane)) = b2;
+    if (lane == 0) {
+      if (p.kv_idx64) reinterpret_cast<int64_t*>(const_cast<void*>(p.kv_indices))[g] = dst;
+      else reinterpret_cast<int32_t*>(const_cast<void*>(p.kv_indices))[g] = (int32_t)dst;
+    }
+  }
+}
+
+int launch_compact(const KernelParams& p, const int64_t* dst_start, int32_t* error_word, void* stream) {
+  // one wave per row, up to kCompactGroups workgroups of 4 waves
+  int64_t groups = (p.max_kv_tokens + kCompactThreads / 64 - 1) / (kCompactThreads / 64);
+  if (groups > kCompactGroups) groups = kCompactGroups;
+  if (groups < 1) groups = 1;
+  hipLaunchKernelGGL(compact_kernel, dim3((unsigned)groups), dim3(kCompactThreads), 0, (hipStream_t)stream, p,
+                     dst_start, error_word);
+  return (int)hipGetLastError();
+}
+
 int launch_meta(const KernelParams& p, const mla_verify_layout_t& lay, void* stream) {
   hipLaunchKernelGGL(meta_kernel, dim3(lay.meta_grid), dim3(kMetaThreads), 0, (hipStream_t)stream, p);
   return (int)hipGetLastError();

@@ -24,7 +24,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert {"mla_verify_plan", "mla_verify_workspace_size", "mla_verify_run"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.mla_verify_abi_version() == 4
+    assert lib.mla_verify_abi_version() == 5
 
 
 def test_struct_layout_matches_header(tmp_path):

@@ -1,0 +1,80 @@
+"""Prefix compaction (KV defragmentation): rows move to contiguous fresh slots,
+kv_indices is rewritten in place, and the verify call on the compacted pool
+gives bit-identical results."""
+import numpy as np
+import pytest
+
+from gpu_helpers import assert_gate, need_gpu, oracle, say
+from workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("idx64", [False, True])
+def test_compaction_moves_rows_and_keeps_results(idx64):
+    torch = need_gpu()
+    from speculative_decoding_mla_page_amd import binding as B
+    from speculative_decoding_mla_page_amd.device import DeviceInputs, Verifier
+    inst = gen.make_instance([3000, 0, 129, 1700], [16, 3, 7, 5], 8, num_slots=16384, seed=98)
+    say(f"compaction idx64={idx64}")
+    di = DeviceInputs(inst, kv_indices_dtype=B.I64 if idx64 else B.I32)
+    # fresh slots after the used pool, poisoned like every unused slot
+    base = inst.num_slots + 32
+    extra = torch.full((32 + inst.total_kv + 32, di.pool.shape[1]), -1, dtype=di.pool.dtype, device=di.pool.device)
+    di.pool = torch.cat([di.pool, extra])
+    di.num_slots = di.pool.shape[0]
+    v = Verifier.for_inputs(di)
+    out, lse = di.alloc_outputs()
+    args = v.args(di, out, lse)
+    B.run(v.plan, args, v.workspace)
+    torch.cuda.synchronize()
+    out0, lse0 = out.cpu().numpy().copy(), lse.cpu().numpy().copy()
+    old = di.kv_indices.cpu().numpy().astype(np.int64)[:inst.total_kv]
+    dst = torch.tensor([base + int(inst.kv_indptr[b]) for b in range(inst.batch)], dtype=torch.int64,
+                       device=di.pool.device)
+    err = torch.zeros(1, dtype=torch.int32, device=di.pool.device)
+    B.compact(v.plan, args, dst, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    new = di.kv_indices.cpu().numpy().astype(np.int64)[:inst.total_kv]
+    assert np.array_equal(new, base + np.arange(inst.total_kv))
+    moved = di.pool[torch.from_numpy(new).to(di.pool.device)][:, :576].cpu().numpy().view(np.uint16)
+    assert np.array_equal(moved, inst.pool_view()[old][:, :576])
+    out.fill_(float("nan"))
+    B.run(v.plan, args, v.workspace)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), out0.view(np.uint32))
+    assert np.array_equal(lse.cpu().numpy().view(np.uint32), lse0.view(np.uint32))
+    ref_out, ref_lse, _ = oracle(inst)
+    assert_gate(out.cpu().numpy(), lse.cpu().numpy(), ref_out, ref_lse, label="compacted")
+
+
+def test_compaction_out_of_pool_destination_is_refused():
+    torch = need_gpu()
+    from speculative_decoding_mla_page_amd import binding as B
+    from speculative_decoding_mla_page_amd.device import DeviceInputs, Verifier
+    inst = gen.make_instance([500, 200], [4, 4], 8, num_slots=4096, seed=99)
+    say("compaction out of pool")
+    di = DeviceInputs(inst)
+    extra = torch.full((600, di.pool.shape[1]), -1, dtype=di.pool.dtype, device=di.pool.device)
+    di.pool = torch.cat([di.pool, extra])
+    di.num_slots = di.pool.shape[0]
+    v = Verifier.for_inputs(di)
+    out, lse = di.alloc_outputs()
+    args = v.args(di, out, lse)
+    before = di.kv_indices.cpu().numpy().copy()
+    # request 0 moves to fresh slots; request 1's range would run past the
+    # pool end: its first 50 rows move, the rest stay where they are
+    dst = torch.tensor([inst.num_slots, di.num_slots - 50], dtype=torch.int64, device=di.pool.device)
+    err = torch.zeros(1, dtype=torch.int32, device=di.pool.device)
+    B.compact(v.plan, args, dst, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == B.DEVERR_SLOT_RANGE
+    after = di.kv_indices.cpu().numpy()
+    k1 = int(inst.kv_indptr[1])
+    assert np.array_equal(after[:k1], inst.num_slots + np.arange(k1))
+    dst1 = di.num_slots - 50 + np.arange(inst.total_kv - k1)
+    ok = dst1 < di.num_slots
+    assert ok.sum() == 50
+    assert np.array_equal(after[k1:inst.total_kv][ok], dst1[ok])
+    assert np.array_equal(after[k1:inst.total_kv][~ok], before[k1:inst.total_kv][~ok])
