@@ -73,6 +73,38 @@ __device__ __forceinline__ int64_t load_index(const void* base, int64_t i, int i
 // indptrs are out of range is skipped (workgroup 0 flags it and plans no
 // work); every read stays inside the ranges the indptrs were checked against.
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// packed tree visibility (metadata launch, the slot-staging workgroups): bit k
+// of token t's word is its mask entry for tree node k of its request, one
+// wave per token: lane k reads entry k and a ballot packs the row.  Square
+// T x T blocks, or full rows of P + T entries whose tree part starts at
+// column P.  Requests whose indptrs or mask size are out of range are
+// skipped (workgroup 0 flags them and plans no work).
+// ---------------------------------------------------------------------------
+__device__ void tree_words(const KernelParams& p, int group, int groups, const int* s_q0, const int* s_P,
+                           const int* s_N, const int* s_tm0, bool full_rows) {
+  const int B = p.batch;
+  const int qB = p.qo_indptr[B];
+  if (qB <= 0 || qB > p.max_q_tokens) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kW = kMetaThreads / 64;
+  for (int t = group * kW + wave; t < qB; t += groups * kW) {
+    int lo = 0, hi = B - 1;   // last request whose tokens start at or before t
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_q0[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int m0 = s_tm0[lo];
+    const int T = s_N[lo] - s_P[lo];
+    const int i = t - s_q0[lo];
+    if (m0 < 0 || i < 0 || i >= T) continue;
+    const int stride = full_rows ? s_P[lo] + T : T;
+    const bool vis = lane < T && p.custom_mask[(size_t)m0 + (size_t)i * stride + lane] != 0;
+    const uint64_t w = __builtin_amdgcn_ballot_w64(vis);
+    if (lane == 0) p.anc[t] = w;
+  }
+}
+
 __device__ void stage_slots(const KernelParams& p, int group, int groups) {
   const int B = p.batch;
   if (B <= 0) return;
@@ -82,16 +114,18 @@ __device__ void stage_slots(const KernelParams& p, int group, int groups) {
   const int total = qB + kB;
   const int per = (total + groups - 1) / groups;
   const int g0 = group * per, g1 = min(total, g0 + per);
-  if (g0 >= g1) return;
   // per request, in LDS: where its keys start, its prefix start and length,
   // its first query token and key count (0 for a request whose indptrs are
   // out of range)
   __shared__ int s_start[kMaxBatch], s_k0[kMaxBatch], s_P[kMaxBatch], s_q0[kMaxBatch], s_N[kMaxBatch];
   __shared__ int s_m0[kMaxBatch];   // full-row mask block of the request, -1 when not checked
+  __shared__ int s_tm0[kMaxBatch];  // tree columns of its node 0's mask row, -1 when unreadable
   const bool check_prefix = (p.flags & MLA_VERIFY_FLAG_CHECK_PREFIX_MASK) != 0;
+  const bool full_rows = (p.flags & MLA_VERIFY_FLAG_MASK_FULL_ROWS) != 0;
   for (int b = threadIdx.x; b < B; b += kMetaThreads) {
     const int q0 = p.qo_indptr[b], q1 = p.qo_indptr[b + 1];
     const int k0 = p.kv_indptr[b], k1 = p.kv_indptr[b + 1];
+    const int m0 = p.mask_indptr[b], m1 = p.mask_indptr[b + 1];
     const bool ok = q0 >= 0 && q1 >= q0 && q1 <= p.max_q_tokens && k0 >= 0 && k1 >= k0 &&
                     (int64_t)k1 <= p.max_kv_tokens;
     s_start[b] = k0 + q0;
@@ -99,13 +133,16 @@ __device__ void stage_slots(const KernelParams& p, int group, int groups) {
     s_P[b] = k1 - k0;
     s_q0[b] = q0;
     s_N[b] = ok ? (k1 - k0) + (q1 - q0) : 0;
-    // the prefix columns are read only where the block has its full size
-    const int m0 = check_prefix ? p.mask_indptr[b] : -1;
-    const int m1 = check_prefix ? p.mask_indptr[b + 1] : -1;
-    const long long full = (long long)(q1 - q0) * ((long long)(k1 - k0) + (q1 - q0));
-    s_m0[b] = (check_prefix && ok && m0 >= 0 && (long long)m1 - m0 == full) ? m0 : -1;
+    // mask rows are read only where the block has the size its layout gives
+    const long long T = q1 - q0;
+    const long long sq = T * T, full = T * ((long long)(k1 - k0) + T);
+    const bool m_ok = ok && m0 >= 0 && (long long)m1 - m0 == (full_rows ? full : sq);
+    s_m0[b] = (check_prefix && full_rows && m_ok) ? m0 : -1;
+    s_tm0[b] = (m_ok && T <= p.max_tree_nodes && T <= 64) ? m0 + (full_rows ? k1 - k0 : 0) : -1;
   }
   __syncthreads();
+  tree_words(p, group, groups, s_q0, s_P, s_N, s_tm0, full_rows);
+  if (g0 >= g1) return;
   // kPer positions per thread at a time: every index load is issued before
   // the first store
   constexpr int kPer = 4;
@@ -183,10 +220,14 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
   __shared__ uint32_t s_err;
   __shared__ long long s_work;
   __shared__ int s_rowblocks;
+  constexpr int kCands = 5;
   __shared__ int s_scan[kMetaThreads];
-  __shared__ int s_cand_items[5];
+  __shared__ int s_cand[kCands];
+  __shared__ int s_cand_items[kCands];
+  __shared__ long long s_cand_cost[kCands];
   __shared__ int32_t s_chunk;
   __shared__ int32_t s_items;
+  __shared__ int32_t s_total_q;
   const int tid = threadIdx.x;
   const int B = p.batch;
   const int H = p.num_heads;
@@ -195,9 +236,14 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
     s_work = 0;
     s_rowblocks = 0;
     s_items = 0;
-    for (int m = 0; m < 5; ++m) s_cand_items[m] = 0;
+    for (int m = 0; m < kCands; ++m) s_cand_items[m] = 0;
   }
   __syncthreads();
+  if (tid == 0) {
+    // query tokens of the call, clamped to the plan's bound
+    int tq = B > 0 ? p.qo_indptr[B] : 0;
+    s_total_q = tq < 0 ? 0 : (tq > p.max_q_tokens ? p.max_q_tokens : tq);
+  }
 
   // per-request lengths and checks (prefix length = kv_indptr[b+1] - kv_indptr[b])
   const bool full_rows = (p.flags & MLA_VERIFY_FLAG_MASK_FULL_ROWS) != 0;
@@ -238,24 +284,26 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
   // rounded up to whole tiles; the one chosen has the least modelled time:
   // rounds of target_items workgroups x (tiles per range + the per-item
   // cost, about kItemTiles tiles), among those whose items fit the plan.
-  auto chunk_for = [&](long long slots) {
-    if (slots < 1) slots = 1;
-    const long long per_item = (s_work + slots - 1) / slots;
-    long long c = ((per_item + kKeysPerTile - 1) / kKeysPerTile) * kKeysPerTile;
-    if (c < kMinChunkKeys) c = kMinChunkKeys;
-    if (c > (1LL << 30)) c = 1LL << 30;
-    return (int)c;
-  };
+  // Thread m works out candidate m, so the 64-bit divisions run side by side.
   auto items_of = [&](int b, int c) {
     const int N = s_req[b][RQ_P] + s_req[b][RQ_T];
     const int rb = s_req[b][RQ_RB];
     return rb > 0 ? rb * ((N + c - 1) / c) : 0;
   };
-  constexpr int kCands = 5;
   constexpr long long kItemTiles = 6;
+  if (tid < kCands) {
+    long long slots = tid == 0 ? (long long)p.target_items : (long long)tid * p.target_items - s_rowblocks;
+    if (slots < 1) slots = 1;
+    const long long per_item = (s_work + slots - 1) / slots;
+    long long c = ((per_item + kKeysPerTile - 1) / kKeysPerTile) * kKeysPerTile;
+    if (c < kMinChunkKeys) c = kMinChunkKeys;
+    if (c > (1LL << 30)) c = 1LL << 30;
+    s_cand[tid] = (int)c;
+  }
+  __syncthreads();
   int cand[kCands];
-  cand[0] = chunk_for(p.target_items);
-  for (int m = 1; m < kCands; ++m) cand[m] = chunk_for((long long)m * p.target_items - s_rowblocks);
+#pragma unroll
+  for (int m = 0; m < kCands; ++m) cand[m] = s_cand[m];
   {
     int mine[kCands] = {0, 0, 0, 0, 0};
     for (int b = tid; b < B; b += kMetaThreads)
@@ -266,15 +314,21 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
       if (mine[m]) atomicAdd(&s_cand_items[m], mine[m]);   // zeroed at the start
   }
   __syncthreads();
+  if (tid < kCands) {
+    // modelled cost of candidate m, -1 when its items do not fit
+    const long long items = s_cand_items[tid];
+    const long long rounds = (items + p.target_items - 1) / p.target_items;
+    s_cand_cost[tid] = items > p.item_capacity ? -1 : (rounds < 1 ? 1 : rounds) * (cand[tid] / kKeysPerTile + kItemTiles);
+  }
+  __syncthreads();
+  // the first candidate of least cost; none fits: cand[0], flagged below
   int chunk_sel = cand[0];
   {
     long long best = -1;
+#pragma unroll
     for (int m = 0; m < kCands; ++m) {
-      const long long items = s_cand_items[m];
-      if (items > p.item_capacity) continue;   // none fits: cand[0], flagged below
-      const long long rounds = (items + p.target_items - 1) / p.target_items;
-      const long long cost = (rounds < 1 ? 1 : rounds) * (cand[m] / kKeysPerTile + kItemTiles);
-      if (best < 0 || cost < best) {
+      const long long cost = s_cand_cost[m];
+      if (cost >= 0 && (best < 0 || cost < best)) {
         best = cost;
         chunk_sel = cand[m];
       }
@@ -346,28 +400,8 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
     e[IT_NROWS] = min(kRowsPerItem, rows - rb * kRowsPerItem);
     e[7] = 0;
   }
-  // packed tree visibility: bit k of node i's word = mask[i][k] != 0
-  const int total_q = bad ? 0 : (B > 0 ? p.qo_indptr[B] : 0);
-  for (int t = tid; t < total_q; t += kMetaThreads) {
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_req[mid][RQ_Q0] <= t) lo = mid; else hi = mid - 1;
-    }
-    // with monotone indptrs the last request starting at or before t holds t
-    const int b = lo;
-    const int T = s_req[b][RQ_T];
-    const int i = t - s_req[b][RQ_Q0];
-    // T x T blocks, or full rows of P + T columns whose tree part starts at P
-    const int Pm = full_rows ? s_req[b][RQ_P] : 0;
-    const uint8_t* row = p.custom_mask + s_req[b][RQ_MASK0] + (size_t)i * (Pm + T) + Pm;
-    uint64_t w = 0;
-    for (int k = 0; k < T; ++k) w |= (uint64_t)(row[k] != 0) << k;
-    p.anc[t] = w;
-  }
   if (tid == 0) {
-    int tq = B > 0 ? p.qo_indptr[B] : 0;
-    tq = tq < 0 ? 0 : (tq > p.max_q_tokens ? p.max_q_tokens : tq);
+    const int tq = s_total_q;
     p.hdr->err = s_err;
     p.hdr->n_items = n_items;
     p.hdr->total_q = tq;
@@ -502,36 +536,20 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
   // 8w..8w+7 (one load).  Keys past the range end re-read the range's last
   // key (finite data, masked).  Loads per tile: 1 (score wave), 4 (PV wave).
   // The slots of a tile are read from LDS one iteration before its loads are
-  // issued (read_slots), so the issue itself never waits on LDS.  Every key
-  // of a tile is a V key of exactly one PV wave, which checks it.
+  // issued (read_slots) and used only when they are issued, after the next
+  // barrier has waited for every LDS read, so neither the read nor the issue
+  // stalls a wave in the middle of its MFMA stream.  Every key of a tile is a
+  // V key of exactly one PV wave, which checks it when it issues its load.
   struct TileSlots {
-    int v[4];     // keys 4r..4r+3 (PV waves, wave-uniform)
-    int rope;     // key 8w + lane / 8 (score waves)
+    int s;   // score waves: the slot of key 8w + lane / 8 (its rope row);
+             // PV waves: the slot of key 4r + (lane & 3)
   };
   auto read_slots = [&](int t) {
-    TileSlots ts;
     const int blk = t / kTilesPerIdx;
     const int32_t* idx = s_idx[blk & 1] - (key0 + blk * kIdxKeys);
     const int jt = key0 + t * kKeysPerTile;
-    if (score_wave) {
-      // the rope key's slot, per lane
-      ts.rope = max(idx[min(jt + 8 * wave + (lane >> 3), key1 - 1)], 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ts.v[i] = 0;
-    } else {
-      // the V keys' slots in one 16-byte broadcast read (4r is 4-aligned
-      // in the block)
-      const i32x4 v4 = *reinterpret_cast<const i32x4*>(idx + jt + 4 * r);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int32_t v = __builtin_amdgcn_readfirstlane(v4[i]);
-        hidden |= v == kSlotMaskedPrefix;
-        out_of_pool |= v < 0 && v != kSlotMaskedPrefix;
-        ts.v[i] = max(v, 0);
-      }
-      ts.rope = 0;
-    }
-    return ts;
+    const int j = score_wave ? min(jt + 8 * wave + (lane >> 3), key1 - 1) : jt + 4 * r + (lane & 3);
+    return TileSlots{idx[j]};
   };
   const unsigned char* pool = reinterpret_cast<const unsigned char*>(p.kv_pool);
   const uint32_t row_bytes = (uint32_t)p.kv_row_stride * 2;
@@ -541,12 +559,15 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
     // one key per load: the slot is wave-uniform, so the row address is
     // formed on the scalar unit
     const int kk = 4 * r + i;
-    const unsigned char* row = pool + (uint64_t)(uint32_t)ts.v[i] * row_bytes;
+    const int32_t v = __builtin_amdgcn_readlane(ts.s, i);
+    hidden |= v == kSlotMaskedPrefix;
+    out_of_pool |= v < 0 && v != kSlotMaskedPrefix;
+    const unsigned char* row = pool + (uint64_t)(uint32_t)max(v, 0) * row_bytes;
     dma16_row(row, (uint32_t)(lane ^ vswz(kk)) * 16, lds_addr(s_v + (t % kStages) * kVSlotBytes + kk * kVStride));
   };
   auto issue_rope = [&](int t, const TileSlots& ts) {
     const int kk = 8 * wave + (lane >> 3);
-    const unsigned char* row = pool + (uint64_t)(uint32_t)ts.rope * row_bytes;
+    const unsigned char* row = pool + (uint64_t)(uint32_t)max(ts.s, 0) * row_bytes;
     const int unit = (lane & 7) ^ rswz(kk);
     dma16(row + 2 * kDv + unit * 16, lds_addr(s_r + (t % kRopeSlots) * kRopeSlotBytes + (8 * wave) * 128));
   };
