@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MLA_VERIFY_ABI_VERSION 5
+#define MLA_VERIFY_ABI_VERSION 6
 #define MLA_VERIFY_D_QK 576          /* latent width used by Q.K^T (512 + 64 rope) */
 #define MLA_VERIFY_D_V 512           /* V = latent dims [0, 512) */
 #define MLA_VERIFY_MAX_TREE_NODES 64 /* tree visibility is packed into one 64-bit word */
@@ -183,7 +183,8 @@ typedef struct {
    every offset 256-byte aligned) and the fixed launch shape of the plan. */
 typedef struct {
   uint64_t total_bytes;
-  uint64_t header_offset;     /* uint32 error word, int32 n_items, int32 total_q, int32 chunk_keys, int32 batch */
+  uint64_t header_offset;     /* uint32 error word, int32 n_items, int32 total_q, int32 chunk_keys, int32 batch,
+                                 int32 max_chunks (key ranges of the request with the most) */
   uint64_t request_offset;    /* int32 [max_batch][8]: P, T, q0, kv0, row_blocks, chunks, item_base, mask0 */
   uint64_t anc_offset;        /* uint64 [max_q_tokens]: packed tree visibility of each node */
   uint64_t items_offset;      /* int32 [item_capacity][8]: b, row_block, chunk, key0, key1, row0, nrows, 0 */
@@ -194,6 +195,8 @@ typedef struct {
                                  at kv_indptr[b] + qo_indptr[b] + j: the pool slot, -1 outside the pool,
                                  -2 for a prefix key a checked full-row mask hides */
   uint64_t stats_offset;      /* mla_verify_compare_stats_t written by mla_verify_compare */
+  uint64_t tokens_offset;     /* int32 [max_q_tokens][4]: per query token, its request's first token,
+                                 first work item, row blocks and key ranges (read by the merge) */
   int32_t item_capacity;
   int32_t rows_per_item;      /* query rows (token x head) per work item */
   int32_t keys_per_tile;      /* keys staged per inner-loop step */

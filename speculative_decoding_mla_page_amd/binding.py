@@ -97,6 +97,7 @@ class Layout(ctypes.Structure):
         ("trace_offset", ctypes.c_uint64),
         ("slots_offset", ctypes.c_uint64),
         ("stats_offset", ctypes.c_uint64),
+        ("tokens_offset", ctypes.c_uint64),
         ("item_capacity", ctypes.c_int32),
         ("rows_per_item", ctypes.c_int32),
         ("keys_per_tile", ctypes.c_int32),

@@ -21,7 +21,7 @@ constexpr int kPartialThreads = (kWaves + kPVWaves) * 64;   // score waves + PV 
 constexpr int kMetaThreads = 256;
 constexpr int kMetaKeysPerGroup = 1024;    // slot-staging workgroups: one per this many keys of capacity
 constexpr int kMetaStageGroups = 256;      // ... and at most this many
-constexpr int kMergeThreads = 256;         // 4 waves per output row, each lane 8 of the 512 dims
+constexpr int kMergeThreads = 512;         // 8 waves per output row, each lane 8 of the 512 dims
 constexpr int kMinChunkKeys = 128;         // shortest key range of a work item
 constexpr int kMaxBatch = 1024;            // per-request tables live in LDS of the metadata kernel
 constexpr uint32_t kPlanMagic = 0x5641'4c4du;  // "MLAV"
@@ -37,7 +37,8 @@ struct WsHeader {
   int32_t total_q;
   int32_t chunk_keys;
   int32_t batch;
-  int32_t pad[3];
+  int32_t max_chunks;   // key ranges of the request with the most
+  int32_t pad[2];
 };
 
 constexpr uint32_t kMetaErrMask = MLA_VERIFY_DEVERR_QO_INDPTR | MLA_VERIFY_DEVERR_KV_INDPTR |
@@ -91,6 +92,7 @@ struct KernelParams {
   WsHeader* hdr;
   int32_t* req;
   uint64_t* anc;
+  int32_t* tok;   // [max_q_tokens][4]: request's first token, first item, row blocks, key ranges
   int32_t* items;
   float* part_o;
   float* part_ml;

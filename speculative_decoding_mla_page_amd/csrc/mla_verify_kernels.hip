@@ -74,54 +74,45 @@ __device__ __forceinline__ int64_t load_index(const void* base, int64_t i, int i
 // work); every read stays inside the ranges the indptrs were checked against.
 // ---------------------------------------------------------------------------
 // ---------------------------------------------------------------------------
-// packed tree visibility (metadata launch, the slot-staging workgroups): bit k
-// of token t's word is its mask entry for tree node k of its request, one
-// wave per token: lane k reads entry k and a ballot packs the row.  Square
-// T x T blocks, or full rows of P + T entries whose tree part starts at
-// column P.  Requests whose indptrs or mask size are out of range are
-// skipped (workgroup 0 flags them and plans no work).
+// metadata launch, workgroups 1..: per-key and per-token staging beside the
+// planning in workgroup 0.  Each group takes a contiguous share of the keys
+// and every groups-th token, and reads the index buffers within the ranges
+// the indptrs were checked against; a request whose indptrs or mask size are
+// out of range is skipped (workgroup 0 flags it and plans no work).
+//
+//   slots: every request's keys in combined order (prefix keys from
+//     kv_indices, then its tree nodes' own keys from out_cache_loc), at
+//     kv_indptr[b] + qo_indptr[b] + j, as int32 pool slots; -1 for a slot
+//     outside [0, num_slots), -2 for a prefix key whose full-row mask column
+//     hides it from some node (with the prefix check).  The split-partial
+//     kernel reads one contiguous, checked list per request.
+//   tree words: bit k of token t's word is its mask entry for tree node k of
+//     its request (T x T blocks, or full rows of P + T entries whose tree part
+//     starts at column P); one wave per token, lane k reads entry k and a
+//     ballot packs the row.
+//   fused KV save: draft token t's latent row kv_new[t] goes to pool slot
+//     out_cache_loc[t], 16 bytes per thread (72 per row), before the partial
+//     launch gathers it; slots outside the pool are not stored.
+// The loads of one pass are all issued before the first of them is used, so
+// a group waits for about two memory round trips.
 // ---------------------------------------------------------------------------
-__device__ void tree_words(const KernelParams& p, int group, int groups, const int* s_q0, const int* s_P,
-                           const int* s_N, const int* s_tm0, bool full_rows) {
-  const int B = p.batch;
-  const int qB = p.qo_indptr[B];
-  if (qB <= 0 || qB > p.max_q_tokens) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int kW = kMetaThreads / 64;
-  for (int t = group * kW + wave; t < qB; t += groups * kW) {
-    int lo = 0, hi = B - 1;   // last request whose tokens start at or before t
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_q0[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    const int m0 = s_tm0[lo];
-    const int T = s_N[lo] - s_P[lo];
-    const int i = t - s_q0[lo];
-    if (m0 < 0 || i < 0 || i >= T) continue;
-    const int stride = full_rows ? s_P[lo] + T : T;
-    const bool vis = lane < T && p.custom_mask[(size_t)m0 + (size_t)i * stride + lane] != 0;
-    const uint64_t w = __builtin_amdgcn_ballot_w64(vis);
-    if (lane == 0) p.anc[t] = w;
-  }
-}
-
-__device__ void stage_slots(const KernelParams& p, int group, int groups) {
+constexpr int kRowUnits = kDqk * 2 / 16;   // 16-byte units per latent row
+__device__ void meta_staging(const KernelParams& p, int group, int groups) {
   const int B = p.batch;
   if (B <= 0) return;
-  const int qB = p.qo_indptr[B];
-  const int kB = p.kv_indptr[B];
-  if (qB < 0 || qB > p.max_q_tokens || kB < 0 || (int64_t)kB > p.max_kv_tokens) return;
-  const int total = qB + kB;
-  const int per = (total + groups - 1) / groups;
-  const int g0 = group * per, g1 = min(total, g0 + per);
   // per request, in LDS: where its keys start, its prefix start and length,
   // its first query token and key count (0 for a request whose indptrs are
   // out of range)
   __shared__ int s_start[kMaxBatch], s_k0[kMaxBatch], s_P[kMaxBatch], s_q0[kMaxBatch], s_N[kMaxBatch];
   __shared__ int s_m0[kMaxBatch];   // full-row mask block of the request, -1 when not checked
   __shared__ int s_tm0[kMaxBatch];  // tree columns of its node 0's mask row, -1 when unreadable
+  __shared__ int s_qB, s_kB;
   const bool check_prefix = (p.flags & MLA_VERIFY_FLAG_CHECK_PREFIX_MASK) != 0;
   const bool full_rows = (p.flags & MLA_VERIFY_FLAG_MASK_FULL_ROWS) != 0;
+  if (threadIdx.x == 0) {
+    s_qB = p.qo_indptr[B];
+    s_kB = p.kv_indptr[B];
+  }
   for (int b = threadIdx.x; b < B; b += kMetaThreads) {
     const int q0 = p.qo_indptr[b], q1 = p.qo_indptr[b + 1];
     const int k0 = p.kv_indptr[b], k1 = p.kv_indptr[b + 1];
@@ -141,11 +132,66 @@ __device__ void stage_slots(const KernelParams& p, int group, int groups) {
     s_tm0[b] = (m_ok && T <= p.max_tree_nodes && T <= 64) ? m0 + (full_rows ? k1 - k0 : 0) : -1;
   }
   __syncthreads();
-  tree_words(p, group, groups, s_q0, s_P, s_N, s_tm0, full_rows);
-  if (g0 >= g1) return;
+  const int qB = s_qB, kB = s_kB;
+  if (qB < 0 || qB > p.max_q_tokens || kB < 0 || (int64_t)kB > p.max_kv_tokens) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kW = kMetaThreads / 64;
+
+  // tree word of token t: where this lane's mask entry is, -1 when it has none
+  // (also for a whole row that is not read)
+  auto tree_entry = [&](int t) -> long long {
+    int lo = 0, hi = B - 1;   // last request whose tokens start at or before t
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_q0[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int m0 = s_tm0[lo];
+    const int T = s_N[lo] - s_P[lo];
+    const int i = t - s_q0[lo];
+    if (m0 < 0 || i < 0 || i >= T || lane >= T) return -1;
+    return (long long)m0 + (long long)i * (full_rows ? s_P[lo] + T : T) + lane;
+  };
+  auto tree_row_valid = [&](int t) {
+    // the row is written when its request's mask is readable (lane 0 always
+    // has an entry then, T >= 1)
+    return __builtin_amdgcn_readfirstlane((int)(tree_entry(t) >= 0 ? 1 : 0));
+  };
+  // this wave's first token: its entry is loaded now and packed after the
+  // slot loads below have been issued
+  const int t_first = group * kW + wave;
+  const long long e_first = t_first < qB ? tree_entry(t_first) : -1;
+  const int row_first = t_first < qB ? tree_row_valid(t_first) : 0;
+  const uint8_t m_first = e_first >= 0 ? p.custom_mask[e_first] : 0;
+
+  // fused KV save: this thread's first unit of the new rows (the rest below)
+  const int64_t units = p.kv_new ? (int64_t)qB * kRowUnits : 0;
+  const int64_t u_first = (int64_t)group * kMetaThreads + threadIdx.x;
+  u32x4 sv = u32x4{0u, 0u, 0u, 0u};
+  int64_t sslot = -1;
+  if (u_first < units) {
+    const int t = (int)(u_first / kRowUnits), c = (int)(u_first % kRowUnits);
+    sv = *reinterpret_cast<const u32x4*>(p.kv_new + (int64_t)t * p.kv_new_stride_tok + 8 * c);
+    sslot = load_index(p.out_cache_loc, t, p.ocl_idx64);
+  }
+
+  const int total = qB + kB;
+  const int per = (total + groups - 1) / groups;
+  const int g0 = group * per, g1 = min(total, g0 + per);
   // kPer positions per thread at a time: every index load is issued before
-  // the first store
-  constexpr int kPer = 4;
+  // the first store.  A thread's positions only grow, so the request that
+  // holds one (the last request whose keys start at or before it) is found
+  // by walking forward from the one that held the previous position; the
+  // walk starts at the request of the group's first position.
+  constexpr int kPer = 8;
+  int lo = 0;
+  {
+    int hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_start[mid] <= g0) lo = mid; else hi = mid - 1;
+    }
+  }
+  int r_start = s_start[lo], r_next = lo + 1 < B ? s_start[lo + 1] : INT_MAX;
   for (int base = g0; base < g1; base += kPer * kMetaThreads) {
     int64_t raw[kPer];
     bool have[kPer], hidden[kPer];
@@ -156,12 +202,12 @@ __device__ void stage_slots(const KernelParams& p, int group, int groups) {
       hidden[k] = false;
       raw[k] = 0;
       if (g >= g1) continue;
-      int lo = 0, hi = B - 1;   // last request whose keys start at or before g
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_start[mid] <= g) lo = mid; else hi = mid - 1;
+      while (g >= r_next) {
+        ++lo;
+        r_start = r_next;
+        r_next = lo + 1 < B ? s_start[lo + 1] : INT_MAX;
       }
-      const int j = g - s_start[lo];
+      const int j = g - r_start;
       if (j < 0 || j >= s_N[lo]) continue;
       const int P = s_P[lo];
       raw[k] = j < P ? load_index(p.kv_indices, (int64_t)s_k0[lo] + j, p.kv_idx64)
@@ -182,29 +228,39 @@ __device__ void stage_slots(const KernelParams& p, int group, int groups) {
       if (p.trace) p.trace[g] = raw[k];
     }
   }
+
+  {
+    const uint64_t w = __builtin_amdgcn_ballot_w64(m_first != 0);
+    if (row_first && lane == 0) p.anc[t_first] = w;
+  }
+  for (int t = t_first + groups * kW; t < qB; t += groups * kW) {
+    const long long e = tree_entry(t);
+    const int row = tree_row_valid(t);
+    const bool vis = e >= 0 && p.custom_mask[e] != 0;
+    const uint64_t w = __builtin_amdgcn_ballot_w64(vis);
+    if (row && lane == 0) p.anc[t] = w;
+  }
+
+  uint16_t* pool = const_cast<uint16_t*>(p.kv_pool);
+  for (int64_t u = u_first; u < units; u += (int64_t)groups * kMetaThreads) {
+    if (u != u_first) {
+      const int t = (int)(u / kRowUnits), c = (int)(u % kRowUnits);
+      sv = *reinterpret_cast<const u32x4*>(p.kv_new + (int64_t)t * p.kv_new_stride_tok + 8 * c);
+      sslot = load_index(p.out_cache_loc, t, p.ocl_idx64);
+    }
+    if (sslot < 0 || sslot >= p.num_slots) continue;
+    *reinterpret_cast<u32x4*>(pool + sslot * p.kv_row_stride + 8 * (int)(u % kRowUnits)) = sv;
+  }
 }
 
-// ---------------------------------------------------------------------------
-// fused KV save (metadata launch, the slot-staging workgroups): draft token
-// t's latent row kv_new[t] goes to pool slot out_cache_loc[t], 16 bytes per
-// thread (72 per row), before the partial launch gathers it.  Only tokens of
-// the checked range [0, qo_indptr[B]) and slots inside the pool are stored.
-// ---------------------------------------------------------------------------
-constexpr int kRowUnits = kDqk * 2 / 16;   // 16-byte units per latent row
-__device__ void save_rows(const KernelParams& p, int group, int groups) {
-  const int B = p.batch;
-  if (B <= 0 || p.kv_new == nullptr) return;
-  const int qB = p.qo_indptr[B];
-  if (qB <= 0 || qB > p.max_q_tokens) return;
-  uint16_t* pool = const_cast<uint16_t*>(p.kv_pool);
-  const int64_t units = (int64_t)qB * kRowUnits;
-  for (int64_t u = (int64_t)group * kMetaThreads + threadIdx.x; u < units; u += (int64_t)groups * kMetaThreads) {
-    const int t = (int)(u / kRowUnits), c = (int)(u % kRowUnits);
-    const int64_t slot = load_index(p.out_cache_loc, t, p.ocl_idx64);
-    if (slot < 0 || slot >= p.num_slots) continue;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(p.kv_new + (int64_t)t * p.kv_new_stride_tok + 8 * c);
-    *reinterpret_cast<u32x4*>(pool + slot * p.kv_row_stride + 8 * c) = v;
+// ceil(a / b) for a >= 0, b >= 1: the 32-bit division when both fit, which
+// is several times shorter than the 64-bit one
+__device__ __forceinline__ long long div_up(long long a, long long b) {
+  if (((unsigned long long)a | (unsigned long long)b) >> 31 == 0) {
+    const uint32_t a32 = (uint32_t)a, b32 = (uint32_t)b;
+    return (long long)((a32 + b32 - 1) / b32);
   }
+  return (a + b - 1) / b;
 }
 
 // ---------------------------------------------------------------------------
@@ -212,8 +268,7 @@ __device__ void save_rows(const KernelParams& p, int group, int groups) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
   if (blockIdx.x > 0) {
-    stage_slots(p, blockIdx.x - 1, gridDim.x - 1);
-    save_rows(p, blockIdx.x - 1, gridDim.x - 1);
+    meta_staging(p, blockIdx.x - 1, gridDim.x - 1);
     return;
   }
   __shared__ int32_t s_req[kMaxBatch][8];
@@ -221,13 +276,14 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
   __shared__ long long s_work;
   __shared__ int s_rowblocks;
   constexpr int kCands = 5;
-  __shared__ int s_scan[kMetaThreads];
+  __shared__ int s_scan[kMetaThreads / 64];
   __shared__ int s_cand[kCands];
   __shared__ int s_cand_items[kCands];
   __shared__ long long s_cand_cost[kCands];
   __shared__ int32_t s_chunk;
   __shared__ int32_t s_items;
   __shared__ int32_t s_total_q;
+  __shared__ int32_t s_max_chunks;
   const int tid = threadIdx.x;
   const int B = p.batch;
   const int H = p.num_heads;
@@ -236,6 +292,7 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
     s_work = 0;
     s_rowblocks = 0;
     s_items = 0;
+    s_max_chunks = 0;
     for (int m = 0; m < kCands; ++m) s_cand_items[m] = 0;
   }
   __syncthreads();
@@ -294,7 +351,7 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
   if (tid < kCands) {
     long long slots = tid == 0 ? (long long)p.target_items : (long long)tid * p.target_items - s_rowblocks;
     if (slots < 1) slots = 1;
-    const long long per_item = (s_work + slots - 1) / slots;
+    const long long per_item = div_up(s_work, slots);
     long long c = ((per_item + kKeysPerTile - 1) / kKeysPerTile) * kKeysPerTile;
     if (c < kMinChunkKeys) c = kMinChunkKeys;
     if (c > (1LL << 30)) c = 1LL << 30;
@@ -317,7 +374,7 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
   if (tid < kCands) {
     // modelled cost of candidate m, -1 when its items do not fit
     const long long items = s_cand_items[tid];
-    const long long rounds = (items + p.target_items - 1) / p.target_items;
+    const long long rounds = div_up(items, (long long)p.target_items);
     s_cand_cost[tid] = items > p.item_capacity ? -1 : (rounds < 1 ? 1 : rounds) * (cand[tid] / kKeysPerTile + kItemTiles);
   }
   __syncthreads();
@@ -334,40 +391,52 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
       }
     }
   }
-  // each request's first item: an exclusive scan of the item counts, each
-  // thread taking a contiguous run of requests
+  // each request's first item: an exclusive scan of the item counts over
+  // contiguous runs of requests per thread, inside each wave by shuffles and
+  // across the waves through LDS
   const int run = (B + kMetaThreads - 1) / kMetaThreads;
   const int b_lo = min(B, tid * run), b_hi = min(B, b_lo + run);
   int local = 0;
   for (int b = b_lo; b < b_hi; ++b) local += items_of(b, chunk_sel);
-  s_scan[tid] = local;
+  const int lane = tid & 63, wv = tid >> 6;
+  int incl = local;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) s_scan[wv] = incl;
   __syncthreads();
-  for (int d = 1; d < kMetaThreads; d <<= 1) {
-    const int add = tid >= d ? s_scan[tid - d] : 0;
-    __syncthreads();
-    s_scan[tid] += add;
-    __syncthreads();
+  int before = 0, all_items = 0;
+#pragma unroll
+  for (int w = 0; w < kMetaThreads / 64; ++w) {
+    const int x = s_scan[w];
+    before += w < wv ? x : 0;
+    all_items += x;
   }
   {
-    int at = s_scan[tid] - local;
+    int at = before + incl - local;
+    int most = 0;
     for (int b = b_lo; b < b_hi; ++b) {
       const int N = s_req[b][RQ_P] + s_req[b][RQ_T];
       const int rb = s_req[b][RQ_RB];
-      s_req[b][RQ_CHUNKS] = rb > 0 ? (N + chunk_sel - 1) / chunk_sel : 0;
+      const int chunks = rb > 0 ? (N + chunk_sel - 1) / chunk_sel : 0;
+      s_req[b][RQ_CHUNKS] = chunks;
       s_req[b][RQ_ITEM0] = at;
       at += items_of(b, chunk_sel);
+      most = max(most, chunks);
     }
+    if (most) atomicMax(&s_max_chunks, most);
   }
   __syncthreads();
   if (tid == 0) {
-    int items = s_scan[kMetaThreads - 1];
+    int items = all_items;
     s_chunk = chunk_sel;
     if (items > p.item_capacity) s_err |= MLA_VERIFY_DEVERR_CAPACITY;
     if (s_err & kMetaErrMask) items = 0;
     s_items = items;
   }
   __syncthreads();
-  const bool bad = (s_err & kMetaErrMask) != 0;
   const int chunk = s_chunk;
   const int n_items = s_items;
 
@@ -400,6 +469,18 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
     e[IT_NROWS] = min(kRowsPerItem, rows - rb * kRowsPerItem);
     e[7] = 0;
   }
+  // per query token, for the merge: its request's first token, first item,
+  // row blocks and key ranges (one 16-byte entry, so the merge reads no
+  // request table)
+  for (int t = tid; t < s_total_q; t += kMetaThreads) {
+    int lo = 0, hi = B - 1;   // last request whose tokens start at or before t
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_req[mid][RQ_Q0] <= t) lo = mid; else hi = mid - 1;
+    }
+    *reinterpret_cast<i32x4*>(p.tok + 4 * (size_t)t) =
+        i32x4{s_req[lo][RQ_Q0], s_req[lo][RQ_ITEM0], s_req[lo][RQ_RB], s_req[lo][RQ_CHUNKS]};
+  }
   if (tid == 0) {
     const int tq = s_total_q;
     p.hdr->err = s_err;
@@ -407,6 +488,7 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
     p.hdr->total_q = tq;
     p.hdr->chunk_keys = chunk;
     p.hdr->batch = B;
+    p.hdr->max_chunks = s_max_chunks;
   }
 }
 
@@ -874,121 +956,142 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
 }
 
 // ---------------------------------------------------------------------------
-// merge: one workgroup per query row (token, head).  Wave w combines the
-// row's partials c = w, w + 4, ... (lane = 8 of the 512 dims); the four wave
-// sums are then added in LDS.  Each partial carries (O, m, l) relative to its
-// own reference max m (base-2 units); with m* = max_c m_c the row is
-// sum_c 2^(m_c - m*) O_c / sum_c 2^(m_c - m*) l_c.
+// merge ("The Capture-Safe Kernel", Decision 4): each partial carries (O, m, l)
+// relative to its own reference max m (base-2 units); with m* = max_c m_c a
+// query row (token, head) is sum_c 2^(m_c - m*) O_c / sum_c 2^(m_c - m*) l_c
+// and lse = (m* + log2 L) ln 2.  A row with no visible key: out = 0,
+// lse = -inf.
+// A workgroup of eight waves takes 8 / w consecutive rows, w waves per row,
+// where w (1, 2, 4 or 8) is the fewest waves that cover the longest
+// request's key ranges kMergeUnroll at a time.  Wave s of a row takes its
+// ranges c = s, s + w, ... (lane = 8 of the 512 dims), kMergeUnroll per pass
+// with all their loads in flight, and folds them into a running (m, l, O);
+// the w wave results are combined the same way through LDS.  A row waits
+// for about three memory round trips (header, plan entry, partials).
+// Workgroups past the last row exit at once.
 // ---------------------------------------------------------------------------
+constexpr int kMergeUnroll = 8;
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(KernelParams p) {
   constexpr int kMW = kMergeThreads / 64;
-  __shared__ float s_red[kMW];
-  __shared__ f32x4 s_acc[kMW - 1][2][64];
-  __shared__ float s_l[kMW - 1];
-  const int H = p.num_heads;
-  const int row = blockIdx.x;
-  const int t = row / H, h = row % H;
+  __shared__ f32x4 s_acc[kMW][2][64];
+  __shared__ float s_m[kMW], s_l[kMW];
   const WsHeader* hdr = p.hdr;
-  if (t >= hdr->total_q) return;
+  const uint32_t err = hdr->err;
+  const int total_q = hdr->total_q;
+  const int most = hdr->max_chunks;
+  const int H = p.num_heads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int wpr = 1;   // waves per row
+  while (wpr < kMW && wpr * kMergeUnroll < most) wpr <<= 1;
+  const int rows_per_wg = kMW / wpr;
+  const int row = blockIdx.x * rows_per_wg + wave / wpr;
+  const int sub = wave % wpr;
+  const int t = row / H, h = row % H;
+  if (blockIdx.x * rows_per_wg >= total_q * H) return;   // the whole workgroup is past the last row
+  // a row past the last one does no work but still meets the barrier below
+  const bool live = t < total_q;
   float* outp = p.out + (int64_t)t * p.out_stride_tok + (int64_t)h * p.out_stride_head;
   float* lsep = p.lse ? p.lse + (int64_t)t * p.lse_stride_tok + h : nullptr;
-  if (hdr->err & kMetaErrMask) {
-    if (tid < 128) *reinterpret_cast<f32x4*>(outp + 4 * tid) = f32x4{NAN, NAN, NAN, NAN};
-    if (lsep && tid == 0) *lsep = NAN;
+  if (err & kMetaErrMask) {
+    if (live && sub == 0) {
+      *reinterpret_cast<f32x4*>(outp + 8 * lane) = f32x4{NAN, NAN, NAN, NAN};
+      *reinterpret_cast<f32x4*>(outp + 8 * lane + 4) = f32x4{NAN, NAN, NAN, NAN};
+      if (lsep && lane == 0) *lsep = NAN;
+    }
     return;
   }
-  // request of token t: the last request starting at or before t holds it
-  const int B = hdr->batch;
-  int lo = 0, hi = B - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (p.req[mid * 8 + RQ_Q0] <= t) lo = mid; else hi = mid - 1;
-  }
-  const int32_t* rq = p.req + lo * 8;
-  const int r = (t - rq[RQ_Q0]) * H + h;
+  i32x4 tk = i32x4{0, 0, 0, 0};   // q0, item0, row blocks, chunks
+  if (live) tk = *reinterpret_cast<const i32x4*>(p.tok + 4 * (size_t)t);
+  const int r = (t - tk[0]) * H + h;
   const int rb = r / kRowsPerItem, lr = r % kRowsPerItem;
-  const int chunks = rq[RQ_CHUNKS], rbs = rq[RQ_RB], base = rq[RQ_ITEM0];
-  auto item_of = [&](int c) { return (size_t)(base + c * rbs + rb) * kRowsPerItem + lr; };
+  const int item0 = tk[1], rbs = tk[2], chunks = live ? tk[3] : 0;
+  auto item_of = [&](int c) { return (size_t)(item0 + c * rbs + rb) * kRowsPerItem + lr; };
 
-  float mloc = -INFINITY;
-  for (int c = tid; c < chunks; c += kMergeThreads) mloc = fmaxf(mloc, p.part_ml[item_of(c) * 2]);
-  for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
-  if (lane == 0) s_red[wave] = mloc;
-  __syncthreads();
-  float mstar = s_red[0];
-#pragma unroll
-  for (int w = 1; w < kMW; ++w) mstar = fmaxf(mstar, s_red[w]);
-
+  // fold weights 2^(m_c - M) into a running (M, L, acc); a range with no
+  // visible key (m_c = -inf) adds nothing
+  float M = -INFINITY, L = 0.f;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
-  if (mstar != -INFINITY) {
-    int c = wave;
-    for (; c + 3 * kMW < chunks; c += 4 * kMW) {
-      f32x4 v[4][2];
-      float m[4], l[4];
+  for (int c0 = sub; c0 < chunks; c0 += wpr * kMergeUnroll) {
+    float m[kMergeUnroll], l[kMergeUnroll];
+    f32x4 v[kMergeUnroll][2];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const size_t ix = item_of(c + u * kMW);
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const int c = c0 + u * wpr;
+      m[u] = -INFINITY;
+      l[u] = 0.f;
+      v[u][0] = v[u][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (c < chunks) {
+        const size_t ix = item_of(c);
         m[u] = p.part_ml[ix * 2];
         l[u] = p.part_ml[ix * 2 + 1];
         const float* po = p.part_o + ix * kDv + 8 * lane;
         v[u][0] = *reinterpret_cast<const f32x4*>(po);
         v[u][1] = *reinterpret_cast<const f32x4*>(po + 4);
       }
+    }
+    float mg = M;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float w = __builtin_amdgcn_exp2f(m[u] - mstar);
-        L += w * l[u];
-        acc0 += w * v[u][0];
-        acc1 += w * v[u][1];
+    for (int u = 0; u < kMergeUnroll; ++u) mg = fmaxf(mg, m[u]);
+    if (mg == -INFINITY) continue;
+    const float sc = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mg);
+    L *= sc;
+    acc0 *= sc;
+    acc1 *= sc;
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const float w = m[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[u] - mg);
+      L += w * l[u];
+      acc0 += w * v[u][0];
+      acc1 += w * v[u][1];
+    }
+    M = mg;
+  }
+  if (wpr > 1) {
+    // the row's other waves hand their (M, L, acc) to its first wave
+    if (sub > 0) {
+      s_acc[wave][0][lane] = acc0;
+      s_acc[wave][1][lane] = acc1;
+      if (lane == 0) {
+        s_m[wave] = M;
+        s_l[wave] = L;
       }
     }
-    for (; c < chunks; c += kMW) {
-      const size_t ix = item_of(c);
-      const float w = __builtin_amdgcn_exp2f(p.part_ml[ix * 2] - mstar);
-      L += w * p.part_ml[ix * 2 + 1];
-      const float* po = p.part_o + ix * kDv + 8 * lane;
-      acc0 += w * *reinterpret_cast<const f32x4*>(po);
-      acc1 += w * *reinterpret_cast<const f32x4*>(po + 4);
+    __syncthreads();
+    if (sub > 0 || !live) return;
+    float mstar = M;
+    for (int w = 1; w < wpr; ++w) mstar = fmaxf(mstar, s_m[wave + w]);
+    if (mstar != -INFINITY) {
+      const float s0 = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - mstar);
+      L *= s0;
+      acc0 *= s0;
+      acc1 *= s0;
+      for (int w = 1; w < wpr; ++w) {
+        const float mw = s_m[wave + w];
+        const float sw = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - mstar);
+        L += sw * s_l[wave + w];
+        acc0 += sw * s_acc[wave + w][0][lane];
+        acc1 += sw * s_acc[wave + w][1][lane];
+      }
     }
+    M = mstar;
   }
-  if (wave > 0) {
-    s_acc[wave - 1][0][lane] = acc0;
-    s_acc[wave - 1][1][lane] = acc1;
-    if (lane == 0) s_l[wave - 1] = L;
-  }
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int w = 0; w < kMW - 1; ++w) {
-    acc0 += s_acc[w][0][lane];
-    acc1 += s_acc[w][1][lane];
-    L += s_l[w];
-  }
+  if (!live) return;
   f32x4 r0, r1;
   float lse;
-  if (mstar == -INFINITY) {
+  if (M == -INFINITY) {
     r0 = r1 = f32x4{0.f, 0.f, 0.f, 0.f};
     lse = -INFINITY;
   } else {
     const float inv = 1.f / L;
     r0 = acc0 * inv;
     r1 = acc1 * inv;
-    lse = (mstar + __builtin_amdgcn_logf(L)) * 0.69314718055994531f;
+    lse = (M + __builtin_amdgcn_logf(L)) * 0.69314718055994531f;
   }
   *reinterpret_cast<f32x4*>(outp + 8 * lane) = r0;
   *reinterpret_cast<f32x4*>(outp + 8 * lane + 4) = r1;
   if (lsep && lane == 0) *lsep = lse;
 }
 
-// ---------------------------------------------------------------------------
-// ---------------------------------------------------------------------------
-// shadow comparison: one workgroup of 128 threads per query row (token,
-// head), 4 output elements per thread, against the caller's reference.
-// Per-row partial statistics are combined in LDS, then added into the
-// workspace stats (zeroed by the metadata launch) with global atomics; the
-// maxima are non-negative floats, compared as their bit patterns.
 // ---------------------------------------------------------------------------
 constexpr int kCompareThreads = 128;
 __device__ __forceinline__ float bf16_ulp_at(float r) {

@@ -24,7 +24,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert {"mla_verify_plan", "mla_verify_workspace_size", "mla_verify_run"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.mla_verify_abi_version() == 5
+    assert lib.mla_verify_abi_version() == 6
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -189,3 +189,6 @@ def test_mask_layout_flags_plan():
     lay = B.layout(_plan(flags=B.FLAG_MASK_FULL_ROWS | B.FLAG_CHECK_PREFIX_MASK))
     assert lay.stats_offset % 256 == 0 and lay.stats_offset >= lay.slots_offset + (1_480_000 + 512) * 4
     assert lay.total_bytes >= lay.stats_offset + ctypes.sizeof(B.CompareStats)
+    # the merge's per-token table comes last
+    assert lay.tokens_offset % 256 == 0 and lay.tokens_offset >= lay.stats_offset + ctypes.sizeof(B.CompareStats)
+    assert lay.total_bytes == lay.tokens_offset + 512 * 16
