@@ -197,6 +197,8 @@ typedef struct {
   uint64_t stats_offset;      /* mla_verify_compare_stats_t written by mla_verify_compare */
   uint64_t tokens_offset;     /* int32 [max_q_tokens][4]: per query token, its request's first token,
                                  first work item, row blocks and key ranges (read by the merge) */
+  uint64_t launch_offset;     /* int32 [partial_grid][8]: per split-partial workgroup, its item (-1: none),
+                                 key0, key1, row0, nrows, and its request's P, q0, kv0 + q0 */
   int32_t item_capacity;
   int32_t rows_per_item;      /* query rows (token x head) per work item */
   int32_t keys_per_tile;      /* keys staged per inner-loop step */

@@ -98,6 +98,7 @@ class Layout(ctypes.Structure):
         ("slots_offset", ctypes.c_uint64),
         ("stats_offset", ctypes.c_uint64),
         ("tokens_offset", ctypes.c_uint64),
+        ("launch_offset", ctypes.c_uint64),
         ("item_capacity", ctypes.c_int32),
         ("rows_per_item", ctypes.c_int32),
         ("keys_per_tile", ctypes.c_int32),

@@ -104,6 +104,8 @@ KernelParams make_params(const PlanImpl& pl, const mla_verify_args_t* a, void* w
   p.slots = reinterpret_cast<int32_t*>(base + l.slots_offset);
   p.stats = reinterpret_cast<mla_verify_compare_stats_t*>(base + l.stats_offset);
   p.tok = reinterpret_cast<int32_t*>(base + l.tokens_offset);
+  p.launch = reinterpret_cast<int32_t*>(base + l.launch_offset);
+  p.partial_grid = l.partial_grid;
   p.trace = (c.flags & MLA_VERIFY_FLAG_TRACE_KEYS) ? reinterpret_cast<int64_t*>(base + l.trace_offset)
                                                    : nullptr;
   return p;
@@ -212,6 +214,8 @@ mla_verify_status_t mla_verify_plan(const mla_verify_config_t* cfg, mla_verify_p
   off = align_up(off + sizeof(mla_verify_compare_stats_t));
   l.tokens_offset = off;
   off = align_up(off + (uint64_t)c.max_q_tokens * 4 * sizeof(int32_t));
+  l.launch_offset = off;
+  off = align_up(off + (uint64_t)l.partial_grid * 8 * sizeof(int32_t));
   l.total_bytes = off;
 
   memset(plan, 0, sizeof(*plan));

@@ -93,6 +93,8 @@ struct KernelParams {
   int32_t* req;
   uint64_t* anc;
   int32_t* tok;   // [max_q_tokens][4]: request's first token, first item, row blocks, key ranges
+  int32_t* launch;   // [partial_grid][8]: item (-1: none), key0, key1, row0, nrows, P, q0, slot base
+  int32_t partial_grid;
   int32_t* items;
   float* part_o;
   float* part_ml;

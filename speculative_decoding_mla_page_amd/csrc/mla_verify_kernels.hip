@@ -444,8 +444,20 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) p.req[b * 8 + c] = s_req[b][c];
   }
-  // work items: request, row block, key range [key0, key1) in combined order
-  for (int it = tid; it < n_items; it += kMetaThreads) {
+  // work items: request, row block, key range [key0, key1) in combined order,
+  // and for every split-partial workgroup its launch entry.  Workgroup g runs
+  // on XCD g % 8 and takes item (g % 8) * per_xcd + g / 8, so the items of a
+  // key range (consecutive, one per row block) share that XCD's L2; the entry
+  // holds all the item's fields the workgroup needs, so it starts with one
+  // load.
+  const int per_xcd = (n_items + 7) >> 3;
+  for (int g = tid; g < p.partial_grid; g += kMetaThreads) {
+    const int it = (g & 7) * per_xcd + (g >> 3);
+    int32_t* ln = p.launch + (size_t)g * 8;
+    if ((g >> 3) >= per_xcd || it >= n_items) {
+      *reinterpret_cast<i32x4*>(ln) = i32x4{-1, 0, 0, 0};
+      continue;
+    }
     int lo = 0, hi = B - 1;
     while (lo < hi) {  // last request whose first item is <= it
       const int mid = (lo + hi + 1) >> 1;
@@ -459,15 +471,14 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
     const int key0 = c * chunk;
     const int key1 = min(N, key0 + chunk);
     const int rows = s_req[b][RQ_T] * H;
+    const int row0 = rb * kRowsPerItem;
+    const int nrows = min(kRowsPerItem, rows - row0);
     int32_t* e = p.items + (size_t)it * 8;
-    e[IT_B] = b;
-    e[IT_RB] = rb;
-    e[IT_CHUNK] = c;
-    e[IT_KEY0] = key0;
-    e[IT_KEY1] = key1;
-    e[IT_ROW0] = rb * kRowsPerItem;
-    e[IT_NROWS] = min(kRowsPerItem, rows - rb * kRowsPerItem);
-    e[7] = 0;
+    *reinterpret_cast<i32x4*>(e) = i32x4{b, rb, c, key0};
+    *reinterpret_cast<i32x4*>(e + 4) = i32x4{key1, row0, nrows, 0};
+    *reinterpret_cast<i32x4*>(ln) = i32x4{it, key0, key1, row0};
+    *reinterpret_cast<i32x4*>(ln + 4) =
+        i32x4{nrows, s_req[b][RQ_P], s_req[b][RQ_Q0], s_req[b][RQ_KV0] + s_req[b][RQ_Q0]};
   }
   // per query token, for the merge: its request's first token, first item,
   // row blocks and key ranges (one 16-byte entry, so the merge reads no
@@ -574,18 +585,16 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
   // Work items of one key range sit on one XCD: workgroup b is dispatched to
   // XCD b % 8, so XCD x gets the contiguous items [x*per, (x+1)*per) and the
   // row blocks that share a key range share that XCD's L2.
-  const int n_items = p.hdr->n_items;
-  const int per_xcd = (n_items + 7) >> 3;
+  // this workgroup's launch entry (written by the metadata launch, which
+  // places the items of a key range on one XCD): item, key range, rows, and
+  // its request's prefix length, first token and slot list
   const int bid = blockIdx.x;
-  if ((bid >> 3) >= per_xcd) return;
-  const int item = (bid & 7) * per_xcd + (bid >> 3);
-  if (item >= n_items) return;
-
-  const int32_t* e = p.items + (size_t)item * 8;
-  const int rb = e[IT_RB], key0 = e[IT_KEY0], key1 = e[IT_KEY1];
-  const int nrows = e[IT_NROWS], row0 = e[IT_ROW0];
-  const int32_t* rq = p.req + e[IT_B] * 8;
-  const int P = rq[RQ_P], q0 = rq[RQ_Q0], kv0 = rq[RQ_KV0];
+  const i32x4 la = *reinterpret_cast<const i32x4*>(p.launch + (size_t)bid * 8);
+  const i32x4 lb = *reinterpret_cast<const i32x4*>(p.launch + (size_t)bid * 8 + 4);
+  const int item = la[0];
+  if (item < 0) return;
+  const int key0 = la[1], key1 = la[2], row0 = la[3];
+  const int nrows = lb[0], P = lb[1], q0 = lb[2], slot0 = lb[3];
   const int H = p.num_heads;
   const int ntiles = (key1 - key0 + kKeysPerTile - 1) / kKeysPerTile;
   const int nrt = (nrows + 15) >> 4;            // row tiles with at least one row
@@ -599,7 +608,7 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
 
   const int r_local = 16 * r + n;
   // this request's checked slots, prefix keys then tree nodes
-  const int32_t* kslots = p.slots + (kv0 + q0);
+  const int32_t* kslots = p.slots + slot0;
 
   // ---- slots: blocks of kIdxKeys keys staged in LDS (double buffered) ----
   // The score waves copy the int32 slots of block b straight into LDS, lane

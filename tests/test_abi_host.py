@@ -191,4 +191,6 @@ def test_mask_layout_flags_plan():
     assert lay.total_bytes >= lay.stats_offset + ctypes.sizeof(B.CompareStats)
     # the merge's per-token table comes last
     assert lay.tokens_offset % 256 == 0 and lay.tokens_offset >= lay.stats_offset + ctypes.sizeof(B.CompareStats)
-    assert lay.total_bytes == lay.tokens_offset + 512 * 16
+    # then the split-partial workgroups' launch entries
+    assert lay.launch_offset % 256 == 0 and lay.launch_offset >= lay.tokens_offset + 512 * 16
+    assert lay.total_bytes == lay.launch_offset + (lay.partial_grid * 32 + 255) // 256 * 256
