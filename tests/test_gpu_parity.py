@@ -56,6 +56,28 @@ def _check_metadata(inst, v, rec):
                 assert e[6] == min(rows_per, t_b * inst.num_heads - rb * rows_per)
                 cover[e[3]:e[4]] += 1
             assert np.all(cover == 1), f"request {b} row block {rb} keys not covered exactly once"
+    # the request table, the merge's per-token entries and the split-partial
+    # launch entries agree with the item table
+    req = v.region(lay.request_offset, max(inst.batch, 1) * 8, torch.int32).cpu().numpy().reshape(-1, 8)
+    chunks = [int(req[b][5]) for b in range(inst.batch)]
+    assert int(hdr[5]) == max(chunks + [0]), "max_chunks in the header"
+    tok = v.region(lay.tokens_offset, max(total_q, 1) * 4, torch.int32).cpu().numpy().reshape(-1, 4)
+    for b in range(inst.batch):
+        for t in range(int(inst.qo_indptr[b]), int(inst.qo_indptr[b + 1])):
+            assert tok[t].tolist() == [int(inst.qo_indptr[b]), int(req[b][6]), int(req[b][4]), chunks[b]], f"token {t}"
+    for b in range(inst.batch):
+        mine = np.nonzero(items[:, 0] == b)[0]
+        if len(mine):
+            assert int(mine.min()) == int(req[b][6]) and len(mine) == int(req[b][4]) * chunks[b]
+    launch = v.region(lay.launch_offset, lay.partial_grid * 8, torch.int32).cpu().numpy().reshape(-1, 8)
+    live = launch[launch[:, 0] >= 0]
+    assert sorted(live[:, 0].tolist()) == list(range(n_items)), "every item launched exactly once"
+    for e in live:
+        it = items[e[0]]
+        b = int(it[0])
+        assert e[1:5].tolist() == [int(it[3]), int(it[4]), int(it[5]), int(it[6])]
+        assert e[5:8].tolist() == [int(inst.prefix_lens[b]), int(inst.qo_indptr[b]),
+                                   int(inst.kv_indptr[b]) + int(inst.qo_indptr[b])]
 
 
 @pytest.mark.parametrize("name", ["tiny", "p5632_t16", "p23040_t32", "p91136_t32"])
@@ -68,6 +90,20 @@ def test_config_parity_full(name):
     ref_out, ref_lse, rec = oracle(inst)
     _check_metadata(inst, v, rec)
     assert_gate(out, lse, ref_out, ref_lse, label=name)
+
+
+def test_many_key_ranges_per_row():
+    """One row block over a 40k-key prefix: about 250 key ranges per query row,
+    so the merge folds its partials over several passes of every wave."""
+    need_gpu()
+    from speculative_decoding_mla_page_amd import binding as B
+    inst = gen.make_instance([40000], [6], 8, num_slots=65536, seed=97)
+    say("many key ranges: P=40000 T=6 H=8")
+    out, lse, v, _ = run_gpu(inst, flags=B.FLAG_TRACE_KEYS)
+    assert int(v.header()[5]) > 128, "expected more key ranges than one pass of eight waves covers"
+    ref_out, ref_lse, rec = oracle(inst)
+    _check_metadata(inst, v, rec)
+    assert_gate(out, lse, ref_out, ref_lse, label="many-ranges")
 
 
 def test_config_parity_h64_sampled():
