@@ -151,7 +151,8 @@ def main():
     inst = gen.config(workload)
     flops, kv_bytes = algorithmic(inst)
     di = DeviceInputs(inst)
-    ver = Verifier.for_inputs(di)
+    # the plan's tree-size bound is the largest draft tree the caller runs
+    ver = Verifier.for_inputs(di, max_tree_nodes=max(1, max(int(t) for t in inst.tree_sizes)))
     out, lse = di.alloc_outputs()
     a = ver.args(di, out, lse)
     stream = torch.cuda.current_stream()

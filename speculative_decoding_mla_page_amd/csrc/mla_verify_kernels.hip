@@ -574,6 +574,11 @@ static_assert(kRowTiles == 1 && kWaves == 4 && kPVWaves == 8, "four score waves 
 static_assert(kPVWaves * 4 == kKeysPerTile, "each PV wave gathers four keys of a tile");
 static_assert(kTilesPerIdx >= 5, "an index block is loaded five tiles ahead of its first use");
 
+// kRowTilesMax: the most 16-row tiles an item of this plan can hold,
+// ceil(min(64, max_tree_nodes x H) / 16); an instantiation for fewer than four
+// (decode: one node per request) leaves out the PV MFMAs and P reads of row
+// tiles that can hold no row.
+template <int kRowTilesMax>
 __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char s_v[kStages * kVSlotBytes];
   __shared__ __attribute__((aligned(16))) unsigned char s_r[kRopeSlots * kRopeSlotBytes];
@@ -919,25 +924,31 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
         alpha4 = s_alpha[(i - 1) & 1][n];
       }
       // PV of tile i - 2, one row tile at a time (row tiles without rows
-      // carry P = 0, so there are no branches but the rare rescale); each P
-      // operand, once used, is replaced by P(i - 1), and in the last pass
-      // each V^T operand by V^T(i)
+      // carry P = 0, so there are no branches but the rare rescale; row tiles
+      // past kRowTilesMax are left out at compile time); each P operand, once
+      // used, is replaced by P(i - 1), and in the last pass each V^T operand
+      // by V^T(i)
 #pragma unroll
       for (int rt = 0; rt < kWaves; ++rt) {
-        if ((resc_cur >> (8 * rt)) & 0xffu) {
-          const float alpha = alpha_cur[rt];
+        if (rt < kRowTilesMax) {
+          if ((resc_cur >> (8 * rt)) & 0xffu) {
+            const float alpha = alpha_cur[rt];
 #pragma unroll
-          for (int dt = 0; dt < kDtPerWave; ++dt) o[dt][rt] *= alpha;
+            for (int dt = 0; dt < kDtPerWave; ++dt) o[dt][rt] *= alpha;
+          }
+#pragma unroll
+          for (int dt = 0; dt < kDtPerWave; ++dt)
+            o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[sv][dt], ph[rt], o[dt][rt], 0, 0, 0);
+#pragma unroll
+          for (int dt = 0; dt < kDtPerWave; ++dt) {
+            o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[sv][dt], pl[rt], o[dt][rt], 0, 0, 0);
+            if (rt == kWaves - 1 && v_next) vt[sv][dt] = v_operand(vslot, dt);
+          }
+          if (p_next) read_p(i - 1, rt);
+        } else if (rt == kWaves - 1 && v_next) {
+#pragma unroll
+          for (int dt = 0; dt < kDtPerWave; ++dt) vt[sv][dt] = v_operand(vslot, dt);
         }
-#pragma unroll
-        for (int dt = 0; dt < kDtPerWave; ++dt)
-          o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[sv][dt], ph[rt], o[dt][rt], 0, 0, 0);
-#pragma unroll
-        for (int dt = 0; dt < kDtPerWave; ++dt) {
-          o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[sv][dt], pl[rt], o[dt][rt], 0, 0, 0);
-          if (rt == kWaves - 1 && v_next) vt[sv][dt] = v_operand(vslot, dt);
-        }
-        if (p_next) read_p(i - 1, rt);
         // the tile loads of this iteration ride along with the MFMAs
         if (rt == 1 && more_dma) {
 #pragma unroll
@@ -1235,8 +1246,15 @@ int launch_meta(const KernelParams& p, const mla_verify_layout_t& lay, void* str
 }
 
 int launch_partial(const KernelParams& p, const mla_verify_layout_t& lay, void* stream) {
-  hipLaunchKernelGGL(partial_kernel, dim3(lay.partial_grid), dim3(kPartialThreads), 0,
-                     (hipStream_t)stream, p);
+  // the most rows an item of this plan holds bound its 16-row tiles
+  const int64_t rows = (int64_t)p.max_tree_nodes * p.num_heads;
+  const int tiles = rows >= kRowsPerItem ? kWaves : (int)((rows + 15) / 16);
+  if (tiles <= 1)
+    hipLaunchKernelGGL(partial_kernel<1>, dim3(lay.partial_grid), dim3(kPartialThreads), 0, (hipStream_t)stream, p);
+  else if (tiles == 2)
+    hipLaunchKernelGGL(partial_kernel<2>, dim3(lay.partial_grid), dim3(kPartialThreads), 0, (hipStream_t)stream, p);
+  else
+    hipLaunchKernelGGL(partial_kernel<kWaves>, dim3(lay.partial_grid), dim3(kPartialThreads), 0, (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
 

@@ -106,6 +106,24 @@ def test_many_key_ranges_per_row():
     assert_gate(out, lse, ref_out, ref_lse, label="many-ranges")
 
 
+@pytest.mark.parametrize("max_nodes,prefixes,trees", [
+    (1, [700, 1500, 33, 4000], [1, 1, 1, 1]),      # 8 rows per request: one row tile
+    (2, [700, 1500, 0, 129], [2, 1, 2, 2]),        # up to 16 rows: one row tile
+    (4, [256, 3000, 77], [4, 3, 4]),               # up to 32 rows: two row tiles
+])
+def test_small_tree_plans(max_nodes, prefixes, trees):
+    """Plans whose tree-size bound keeps every item under 64 rows run the
+    split-partial instantiation without the empty row tiles' PV work."""
+    need_gpu()
+    from speculative_decoding_mla_page_amd import binding as B
+    inst = gen.make_instance(prefixes, trees, 8, num_slots=16384, seed=90 + max_nodes)
+    say(f"small tree plan: max_tree_nodes={max_nodes} P={prefixes} T={trees}")
+    out, lse, v, _ = run_gpu(inst, flags=B.FLAG_TRACE_KEYS, max_tree_nodes=max_nodes)
+    ref_out, ref_lse, rec = oracle(inst)
+    _check_metadata(inst, v, rec)
+    assert_gate(out, lse, ref_out, ref_lse, label=f"max_tree_nodes={max_nodes}")
+
+
 def test_config_parity_h64_sampled():
     """H = 64 (2,048 query rows): oracle on sampled tree nodes."""
     need_gpu()
