@@ -38,7 +38,19 @@ DESCRIPTIONS = {
                       "576-d bf16 latent, page_size=1 pool of 262,144 slots, fp32 out + LSE",
     "decode_b64_h128": "decode: 64 requests x 1 query token, prefixes U[512, 8192] (292,951 keys), H=128, "
                        "576-d bf16 latent, page_size=1 pool of 524,288 slots, fp32 out + LSE",
+    "p91136_t32_h64": "1 request, 91,136-token prefix, 32-node random tree, H=64 (2,048 query rows), 576-d bf16 "
+                      "latent (V = first 512), 1% outlier rows x8, page_size=1 pool of 1,048,576 slots, "
+                      "fp32 out + LSE",
+    "p23040_t32": "1 request, 23,040-token prefix, 32-node random tree, H=8, 576-d bf16 latent (V = first 512), "
+                  "page_size=1 pool of 262,144 slots, fp32 out + LSE",
+    "p5632_t16": "1 request, 5,632-token prefix, 16-node random tree, H=8, 576-d bf16 latent (V = first 512), "
+                 "page_size=1 pool of 65,536 slots, fp32 out + LSE",
 }
+GRAPH_WORKLOAD = "segmented_b8_graph"
+DESCRIPTIONS[GRAPH_WORKLOAD] = (
+    "segmented batch: 8 requests, prefixes U[1000, 185000], trees U[8, 64] (random parents), H=8, 576-d bf16 "
+    "latent, fully populated 2,097,152-slot pool; one hipGraph capture, replayed with the indptrs, kv_indices, "
+    "out_cache_loc, masks and queries rewritten in place before each replay (fresh draws, seeds 2000 + r)")
 
 
 def traffic_file(workload: str) -> str:
@@ -148,6 +160,9 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     workload = args.workload
+    if workload == GRAPH_WORKLOAD:
+        bench_graph(args)
+        return
     inst = gen.config(workload)
     flops, kv_bytes = algorithmic(inst)
     di = DeviceInputs(inst)
@@ -344,6 +359,131 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inst, kv_bytes, workload)
+    print(json.dumps(result), flush=True)
+
+
+def bench_graph(args):
+    """The segmented batch under hipGraph replay: the call is captured once on
+    buffers sized to the plan bounds; before each replay one of R fresh draws
+    is copied into them (host to device, stream-ordered, outside the timed
+    span), and events bracket the replay alone.  The value is the gathered
+    latent bytes of all timed replays over their summed time."""
+    import numpy as np
+    import torch
+    from speculative_decoding_mla_page_amd import binding as B
+    from speculative_decoding_mla_page_amd.device import Verifier
+    from workloads import gen
+
+    dev = torch.device("cuda")
+    bounds = gen.SEGMENTED_BOUNDS
+    h = gen.SEGMENTED["num_heads"]
+    pool = torch.from_numpy(gen.segmented_pool().view(np.int16)).to(dev)
+    mq = bounds["max_q_tokens"]
+    static = {
+        "q": torch.zeros((mq, h, 576), dtype=torch.int16, device=dev),
+        "qo_indptr": torch.zeros(bounds["max_batch"] + 1, dtype=torch.int32, device=dev),
+        "kv_indptr": torch.zeros(bounds["max_batch"] + 1, dtype=torch.int32, device=dev),
+        "mask_indptr": torch.zeros(bounds["max_batch"] + 1, dtype=torch.int32, device=dev),
+        "kv_indices": torch.zeros(bounds["max_kv_tokens"], dtype=torch.int32, device=dev),
+        "out_cache_loc": torch.zeros(mq, dtype=torch.int64, device=dev),
+        "custom_mask": torch.zeros(mq * bounds["max_tree_nodes"], dtype=torch.uint8, device=dev),
+    }
+    out = torch.zeros((mq, h, 512), dtype=torch.float32, device=dev)
+    lse = torch.zeros((mq, h), dtype=torch.float32, device=dev)
+    ver = Verifier(h, bounds["max_batch"], mq, bounds["max_kv_tokens"], max_tree_nodes=bounds["max_tree_nodes"])
+    a = B.make_args(gen.SEGMENTED["batch"], float(gen.SM_SCALE), static["q"], pool, static["qo_indptr"],
+                    static["kv_indptr"], static["kv_indices"], static["out_cache_loc"], static["custom_mask"],
+                    static["mask_indptr"], out, lse)
+
+    n_draws = max(1, min(args.steps, 25))
+    draws = []
+    for r in range(n_draws):
+        rep = gen.segmented_replay(r)
+        host = {k: torch.from_numpy(np.ascontiguousarray(v)).reshape(-1)
+                for k, v in (("qo_indptr", rep.qo_indptr), ("kv_indptr", rep.kv_indptr),
+                             ("mask_indptr", rep.mask_indptr), ("kv_indices", rep.kv_indices),
+                             ("out_cache_loc", rep.out_cache_loc), ("custom_mask", rep.custom_mask))}
+        host["q"] = torch.from_numpy(rep.q.view(np.int16))
+        flops = sum(2 * t * h * (pp + t) * (576 + 512) for pp, t in zip(rep.prefix_lens, rep.tree_sizes))
+        kv_bytes = (rep.total_kv + rep.total_q) * 1152
+        draws.append((host, flops, kv_bytes))
+
+    def fill(host):
+        for k, t in host.items():
+            if k == "q":
+                static["q"][:t.shape[0]].copy_(t)
+            else:
+                static[k][:t.numel()].copy_(t.view(static[k].dtype))
+
+    fill(draws[0][0])
+    torch.cuda.synchronize()
+    B.run(ver.plan, a, ver.workspace)              # loads the code objects before capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            B.run(ver.plan, a, ver.workspace)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    for w in range(args.warmup):
+        fill(draws[w % n_draws][0])
+        g.replay()
+    torch.cuda.synchronize()
+    if ver.error_word() != 0:
+        raise RuntimeError(f"device error word {ver.error_word():#x}")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    flops_all = bytes_all = 0
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        host, fl, kb = draws[i % n_draws]
+        fill(host)
+        evs[i][0].record(stream)
+        g.replay()
+        evs[i][1].record(stream)
+        flops_all += fl
+        bytes_all += kb
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if ver.error_word() != 0:
+        raise RuntimeError(f"device error word {ver.error_word():#x}")
+    rep_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    total_s = float(rep_ms.sum()) * 1e-3
+    t_hbm = bytes_all / (PEAK_HBM_GBS * 1e9)
+    t_mfma = flops_all / (PEAK_MFMA_BF16_TFLOPS * 1e12)
+    bound = "mfma" if t_mfma >= t_hbm else "hbm"
+    achieved = (flops_all / total_s / 1e12) if bound == "mfma" else (bytes_all / total_s / 1e9)
+    peak = PEAK_MFMA_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS
+    result = {
+        "metric": f"µs/call + effective KV GB/s & %roofline, {GRAPH_WORKLOAD}",
+        "value": bytes_all / total_s / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": DESCRIPTIONS[GRAPH_WORKLOAD], "name": GRAPH_WORKLOAD,
+                   "batch": gen.SEGMENTED["batch"], "heads": h, "distinct_draws": n_draws,
+                   "mean_keys_per_replay": bytes_all / 1152 / args.steps},
+        "us_per_call": float(rep_ms.mean() * 1e3),
+        "us_per_call_each_p10_p50_p90": [float(np.percentile(rep_ms, q) * 1e3) for q in (10, 50, 90)],
+        "tflops_per_call": flops_all / total_s / 1e12,
+        "algorithmic": {"flops_per_call": flops_all / args.steps, "kv_bytes_per_call": bytes_all / args.steps},
+        "roofline": {"bound": bound, "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "frac": achieved / peak,
+                     "traffic": None, "kernel": "whole call (graph replay: metadata, partial, merge)"},
+        "roofline_call": {"frac": max(t_hbm, t_mfma) / total_s, "frac_hbm": t_hbm / total_s,
+                          "frac_mfma": t_mfma / total_s},
+        "cpu_baseline": None,
+    }
     print(json.dumps(result), flush=True)
 
 
