@@ -363,11 +363,12 @@ def main():
 
 
 def bench_graph(args):
-    """The segmented batch under hipGraph replay: the call is captured once on
-    buffers sized to the plan bounds; before each replay one of R fresh draws
-    is copied into them (host to device, stream-ordered, outside the timed
-    span), and events bracket the replay alone.  The value is the gathered
-    latent bytes of all timed replays over their summed time."""
+    """The segmented batch under hipGraph replay.  The call is captured twice,
+    on two sets of buffers sized to the plan bounds.  Replay i uses set i % 2;
+    draw i (one of R fresh draws) is copied into that set on a side stream,
+    after replay i - 2 has finished with it and while replay i - 1 still runs.
+    The replay is then queued behind replay i - 1, so the events around it
+    bracket the graph alone (no copy, no host submission gap)."""
     import numpy as np
     import torch
     from speculative_decoding_mla_page_amd import binding as B
@@ -379,21 +380,26 @@ def bench_graph(args):
     h = gen.SEGMENTED["num_heads"]
     pool = torch.from_numpy(gen.segmented_pool().view(np.int16)).to(dev)
     mq = bounds["max_q_tokens"]
-    static = {
-        "q": torch.zeros((mq, h, 576), dtype=torch.int16, device=dev),
-        "qo_indptr": torch.zeros(bounds["max_batch"] + 1, dtype=torch.int32, device=dev),
-        "kv_indptr": torch.zeros(bounds["max_batch"] + 1, dtype=torch.int32, device=dev),
-        "mask_indptr": torch.zeros(bounds["max_batch"] + 1, dtype=torch.int32, device=dev),
-        "kv_indices": torch.zeros(bounds["max_kv_tokens"], dtype=torch.int32, device=dev),
-        "out_cache_loc": torch.zeros(mq, dtype=torch.int64, device=dev),
-        "custom_mask": torch.zeros(mq * bounds["max_tree_nodes"], dtype=torch.uint8, device=dev),
-    }
-    out = torch.zeros((mq, h, 512), dtype=torch.float32, device=dev)
-    lse = torch.zeros((mq, h), dtype=torch.float32, device=dev)
     ver = Verifier(h, bounds["max_batch"], mq, bounds["max_kv_tokens"], max_tree_nodes=bounds["max_tree_nodes"])
-    a = B.make_args(gen.SEGMENTED["batch"], float(gen.SM_SCALE), static["q"], pool, static["qo_indptr"],
-                    static["kv_indptr"], static["kv_indices"], static["out_cache_loc"], static["custom_mask"],
-                    static["mask_indptr"], out, lse)
+
+    def buffers():
+        st = {
+            "q": torch.zeros((mq, h, 576), dtype=torch.int16, device=dev),
+            "qo_indptr": torch.zeros(bounds["max_batch"] + 1, dtype=torch.int32, device=dev),
+            "kv_indptr": torch.zeros(bounds["max_batch"] + 1, dtype=torch.int32, device=dev),
+            "mask_indptr": torch.zeros(bounds["max_batch"] + 1, dtype=torch.int32, device=dev),
+            "kv_indices": torch.zeros(bounds["max_kv_tokens"], dtype=torch.int32, device=dev),
+            "out_cache_loc": torch.zeros(mq, dtype=torch.int64, device=dev),
+            "custom_mask": torch.zeros(mq * bounds["max_tree_nodes"], dtype=torch.uint8, device=dev),
+            "out": torch.zeros((mq, h, 512), dtype=torch.float32, device=dev),
+            "lse": torch.zeros((mq, h), dtype=torch.float32, device=dev),
+        }
+        st["args"] = B.make_args(gen.SEGMENTED["batch"], float(gen.SM_SCALE), st["q"], pool, st["qo_indptr"],
+                                 st["kv_indptr"], st["kv_indices"], st["out_cache_loc"], st["custom_mask"],
+                                 st["mask_indptr"], st["out"], st["lse"])
+        return st
+
+    sets = [buffers(), buffers()]
 
     n_draws = max(1, min(args.steps, 25))
     draws = []
@@ -408,30 +414,51 @@ def bench_graph(args):
         kv_bytes = (rep.total_kv + rep.total_q) * 1152
         draws.append((host, flops, kv_bytes))
 
-    def fill(host):
+    def fill(st, host):
         for k, t in host.items():
             if k == "q":
-                static["q"][:t.shape[0]].copy_(t)
+                st["q"][:t.shape[0]].copy_(t)
             else:
-                static[k][:t.numel()].copy_(t.view(static[k].dtype))
+                st[k][:t.numel()].copy_(t.view(st[k].dtype))
 
-    fill(draws[0][0])
-    torch.cuda.synchronize()
-    B.run(ver.plan, a, ver.workspace)              # loads the code objects before capture
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        with torch.cuda.graph(g, stream=side):
-            B.run(ver.plan, a, ver.workspace)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
+    main = torch.cuda.current_stream()
+    graphs = []
+    for st in sets:
+        fill(st, draws[0][0])
+        torch.cuda.synchronize()
+        B.run(ver.plan, st["args"], ver.workspace)     # loads the code objects before capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                B.run(ver.plan, st["args"], ver.workspace)
+        main.wait_stream(side)
+        torch.cuda.synchronize()
+        graphs.append(g)
 
-    stream = torch.cuda.current_stream()
+    copy_stream = torch.cuda.Stream()
+    done = [torch.cuda.Event(), torch.cuda.Event()]
+    for d in done:
+        d.record(main)
+
+    def replay(i, evs=None):
+        k = i % 2
+        host, _, _ = draws[i % n_draws]
+        with torch.cuda.stream(copy_stream):
+            copy_stream.wait_event(done[k])       # replay i - 2 has finished with set k
+            fill(sets[k], host)                   # returns once the copies are done
+        main.wait_stream(copy_stream)
+        if evs is not None:
+            evs[0].record(main)
+        graphs[k].replay()
+        if evs is not None:
+            evs[1].record(main)
+        done[k].record(main)
+
     for w in range(args.warmup):
-        fill(draws[w % n_draws][0])
-        g.replay()
+        replay(w)
     torch.cuda.synchronize()
     if ver.error_word() != 0:
         raise RuntimeError(f"device error word {ver.error_word():#x}")
@@ -439,11 +466,8 @@ def bench_graph(args):
     flops_all = bytes_all = 0
     t0 = time.perf_counter()
     for i in range(args.steps):
-        host, fl, kb = draws[i % n_draws]
-        fill(host)
-        evs[i][0].record(stream)
-        g.replay()
-        evs[i][1].record(stream)
+        replay(args.warmup + i, evs[i])
+        _, fl, kb = draws[(args.warmup + i) % n_draws]
         flops_all += fl
         bytes_all += kb
     torch.cuda.synchronize()
