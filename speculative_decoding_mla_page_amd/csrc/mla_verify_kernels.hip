@@ -678,12 +678,13 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
   const int loads_per_tile = score_wave ? 1 : 4;
 
   // The two roles run separate loops with the same barrier sequence: one
-  // barrier before the first tile, then one barrier A(i) at the top of each
-  // iteration i = 0..ntiles + 1.  Iteration i: scores of tile i and P(i) into
-  // P buffer i & 1 (score waves) || PV of tile i - 2 from registers, P(i - 1)
-  // out of P buffer (i - 1) & 1 and V^T(i) into registers (PV waves).  P(i - 1)
-  // is read in iteration i, before the score waves rewrite its buffer in
-  // iteration i + 1.  Tile i + 2 goes to the V and rope
+  // barrier A(i) at the top of each iteration i = 0..ntiles.  Iteration i:
+  // scores of tile i and P(i) into P buffer i & 1 (score waves) || PV of tile
+  // i - 2 from registers, P(i - 1) out of P buffer (i - 1) & 1 and V^T(i)
+  // into registers (PV waves); in the last one (i = ntiles) the PV waves also
+  // multiply tile ntiles - 1, whose P they have just read.  P(i - 1) is read
+  // in iteration i, before the score waves rewrite its buffer in iteration
+  // i + 1.  Tile i + 2 goes to the V and rope
   // slots of tile i - 1, free since A(i); its slots were read from LDS in
   // iteration i - 1.
   // Index block b lands before tile 8b - 5 (issued after tile 8b - 6), and
@@ -692,12 +693,26 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
   // only: index loads in flight behind a tile make them wait a little longer,
   // never less.
   TileSlots next_slots{};
+  // The slots of tiles 0..2 come straight from the staged list (the same
+  // values, clamped to the range's last key, that the LDS blocks hold), so
+  // the first gathers wait for one load instead of the first slot block and a
+  // barrier.  The first LDS slot read (tile 3, iteration 0) follows A(0),
+  // by which every score wave's first index load has landed.  Loads the
+  // compiler issued (queries, these slots) are older than the tile loads, so
+  // the tile waits only ever wait longer for them.
+  TileSlots pre[3] = {};
+  auto load_pre = [&]() {
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      if (t >= ntiles) break;
+      const int jt = key0 + t * kKeysPerTile;
+      const int j = min(score_wave ? jt + 8 * wave + (lane >> 3) : jt + 4 * r + (lane & 3), key1 - 1);
+      pre[t] = TileSlots{kslots[j]};
+    }
+  };
   auto prologue = [&]() {
-    // nothing the compiler loaded may still be in flight once the loop runs
-    __builtin_amdgcn_s_waitcnt(0);
-    wait_vm_barrier(0);
-    for (int t = 0; t < 2 && t < ntiles; ++t) issue(t, read_slots(t));
-    if (2 < ntiles) next_slots = read_slots(2);
+    for (int t = 0; t < 2 && t < ntiles; ++t) issue(t, pre[t]);
+    if (2 < ntiles) next_slots = pre[2];
   };
   auto barrier_a = [&](int i) {
     // tile i must have landed; tile i + 1 may still be in flight (the last
@@ -719,6 +734,7 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
     const bool s_active = r < nrt;
     // the first slot block is on its way while the queries load
     if (ntiles > 0) issue_idx(0);
+    load_pre();
     bf16x8 qf[kDqk / 32];
     uint64_t anc;
     {
@@ -752,7 +768,7 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
     }
     prologue();
 
-    for (int i = 0; i <= ntiles + 1; ++i) {
+    for (int i = 0; i <= ntiles; ++i) {
       barrier_a(i);
       if (!s_active || i >= ntiles) {
         after_a(i);
@@ -871,6 +887,7 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
       for (int dt = 0; dt < kDtPerWave; ++dt)
         v_lo[dt] = v_key * kVStride + (n & 1) * 8 + ((((kDvPerWave / 8) * r + 2 * dt + ((n >> 1) & 1)) ^ vswz(v_key)) << 4);
     }
+    load_pre();
     prologue();
     // The PV waves run two tiles behind the score waves: iteration i
     // multiplies tile i - 2 with operands that are all in registers by then
@@ -895,6 +912,29 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
 
     // one iteration; the parity of i is a compile-time constant so that the
     // two V^T register sets are addressed statically
+    // PV of the last tile, in the iteration that reads its P (ntiles): its
+    // V^T is in register set sv ^ 1 (read in the iteration before), its P and
+    // rescale factors were loaded in this iteration.  No iteration follows
+    // only to drain the two-tile lag.
+    auto final_pv = [&](auto parity) {
+      constexpr int sv = decltype(parity)::value;
+#pragma unroll
+      for (int rt = 0; rt < kWaves; ++rt) {
+        if (rt < kRowTilesMax) {
+          if ((resc >> (8 * rt)) & 0xffu) {
+            const float alpha = alpha4[rt];
+#pragma unroll
+            for (int dt = 0; dt < kDtPerWave; ++dt) o[dt][rt] *= alpha;
+          }
+#pragma unroll
+          for (int dt = 0; dt < kDtPerWave; ++dt)
+            o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[sv ^ 1][dt], ph[rt], o[dt][rt], 0, 0, 0);
+#pragma unroll
+          for (int dt = 0; dt < kDtPerWave; ++dt)
+            o[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[sv ^ 1][dt], pl[rt], o[dt][rt], 0, 0, 0);
+        }
+      }
+    };
     auto pv_iteration = [&](int i, auto parity) {
       constexpr int sv = decltype(parity)::value;   // = i & 1: V^T(i - 2) in, V^T(i) out
       barrier_a(i);
@@ -913,6 +953,7 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
           for (int rt = 0; rt < kWaves; ++rt) read_p(i - 1, rt);
         }
         after_a(i);
+        if (i == ntiles && ntiles > 0) final_pv(parity);
         return;
       }
       const bool more_dma = i + 2 < ntiles;
@@ -957,10 +998,11 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
         if (rt == 2 && more_slots) next_slots = read_slots(i + 3);
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (i == ntiles) final_pv(parity);
     };
-    for (int i = 0; i <= ntiles + 1; i += 2) {
+    for (int i = 0; i <= ntiles; i += 2) {
       pv_iteration(i, std::integral_constant<int, 0>{});
-      if (i + 1 <= ntiles + 1) pv_iteration(i + 1, std::integral_constant<int, 1>{});
+      if (i + 1 <= ntiles) pv_iteration(i + 1, std::integral_constant<int, 1>{});
     }
     out_of_pool = __syncthreads_or(out_of_pool);
     hidden = __syncthreads_or(hidden);
