@@ -1004,8 +1004,8 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
       pv_iteration(i, std::integral_constant<int, 0>{});
       if (i + 1 <= ntiles) pv_iteration(i + 1, std::integral_constant<int, 1>{});
     }
-    out_of_pool = __syncthreads_or(out_of_pool);
-    hidden = __syncthreads_or(hidden);
+    // the partial O does not depend on the poison flags (a poisoned item's l
+    // is NaN): store it before the flag reductions
 #pragma unroll
     for (int rt = 0; rt < kWaves; ++rt) {
       const int rl = 16 * rt + n;
@@ -1014,6 +1014,8 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
 #pragma unroll
       for (int dt = 0; dt < kDtPerWave; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * g) = o[dt][rt];
     }
+    out_of_pool = __syncthreads_or(out_of_pool);
+    hidden = __syncthreads_or(hidden);
   }
 }
 
