@@ -789,8 +789,9 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
                                           : rslot + 16 * kt * 128 + (ks == 16 ? r_off : r_off2);
         return *reinterpret_cast<const bf16x8*>(ap);
       };
-      // the scores and P gate the next PV step: the score wave goes ahead of
-      // the PV wave on this SIMD until P is written
+      // the scores gate the next PV step: the score wave goes ahead of the PV
+      // waves on its SIMD for the S MFMAs; during its softmax the PV waves
+      // (priority 1) go first and fill the MFMA pipe
       __builtin_amdgcn_s_setprio(3);
       bf16x8 ka[kKRing];
 #pragma unroll
@@ -807,6 +808,7 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
         if (step == 8 && i + 3 < ntiles) next_slots = read_slots(i + 3);
         __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_setprio(0);
       // scores in base-2 units; mask the range tail and invisible tree keys
       const bool need_mask = jt + kKeysPerTile > min(P, key1);
       float mx = -INFINITY;
@@ -856,7 +858,6 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
       s_p[i & 1][r][1][lane] = plo;
       if (any_need && g == 0) s_alpha[i & 1][n][r] = alpha;
       if (lane == 0) reinterpret_cast<uint8_t*>(&s_rescale[i & 1])[r] = any_need;
-      __builtin_amdgcn_s_setprio(0);
     }
     out_of_pool = __syncthreads_or(out_of_pool);
     hidden = __syncthreads_or(hidden);
@@ -935,6 +936,7 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
         }
       }
     };
+    __builtin_amdgcn_s_setprio(1);
     auto pv_iteration = [&](int i, auto parity) {
       constexpr int sv = decltype(parity)::value;   // = i & 1: V^T(i - 2) in, V^T(i) out
       barrier_a(i);
