@@ -284,6 +284,33 @@ mla_verify_status_t mla_verify_compare(const mla_verify_plan_t* plan, const mla_
 mla_verify_status_t mla_verify_compact(const mla_verify_plan_t* plan, const mla_verify_args_t* args,
                                        const int64_t* dst_start, int32_t* error_word, void* stream);
 
+/*
+ * Measurement helper, outside the attention path: enqueues on `stream` one
+ * launch of `blocks` workgroups of four waves; each wave runs `iters` rounds of
+ * four independent bf16 16x16x32 MFMAs (4 x 16,384 flops per round), so one
+ * call performs blocks x 4 x iters x 65,536 flops.  Timing it gives the dense
+ * bf16 MFMA rate reached at the clock the GPU holds under load.
+ *   out   float [blocks x 256], device memory: each thread's accumulator sum
+ *         (exact, so linear in iters, for iters <= 4).
+ * Returns MLA_VERIFY_ERR_INVALID_ARGUMENT for iters < 1, blocks < 1 or a null
+ * or misaligned out, MLA_VERIFY_ERR_LAUNCH if HIP refuses the launch.
+ */
+mla_verify_status_t mla_verify_calibrate_mfma(int32_t iters, int32_t blocks, float* out, void* stream);
+
+/*
+ * Measurement helper, outside the attention path: enqueues on `stream` one
+ * launch of `blocks` workgroups of 256 threads that read every byte of `buf`
+ * once, in 16-byte units at a grid stride, and write one float per thread to
+ * `out` (a checksum of the words it read).  Timing it gives the HBM read rate.
+ *   buf    device memory, 16-byte aligned, `bytes` long (a multiple of 16).
+ *   out    float [blocks x 256], device memory.
+ * Returns MLA_VERIFY_ERR_INVALID_ARGUMENT for a null or misaligned pointer,
+ * bytes < 16 or not a multiple of 16, or blocks < 1; MLA_VERIFY_ERR_LAUNCH if
+ * HIP refuses the launch.
+ */
+mla_verify_status_t mla_verify_calibrate_read(const void* buf, int64_t bytes, int32_t blocks, float* out,
+                                              void* stream);
+
 /* MLA_VERIFY_ABI_VERSION of the built library. */
 int32_t mla_verify_abi_version(void);
 

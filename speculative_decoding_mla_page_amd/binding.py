@@ -159,6 +159,11 @@ def lib() -> ctypes.CDLL:
         l.mla_verify_compact.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args), ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_void_p]
         l.mla_verify_compact.restype = ctypes.c_int
+        l.mla_verify_calibrate_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+        l.mla_verify_calibrate_mfma.restype = ctypes.c_int
+        l.mla_verify_calibrate_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        l.mla_verify_calibrate_read.restype = ctypes.c_int
         l.mla_verify_status_string.argtypes = [ctypes.c_int]
         l.mla_verify_status_string.restype = ctypes.c_char_p
         l.mla_verify_abi_version.argtypes = []
@@ -267,6 +272,29 @@ def compact(p: Plan, args: Args, dst_start, error_word, stream=None) -> None:
                                   _stream(stream))
     if st != OK:
         raise MlaVerifyError(st, "mla_verify_compact")
+
+
+def calibrate_mfma(iters: int, blocks: int, out, stream=None) -> None:
+    """Enqueue the bf16 MFMA loop (blocks x 4 waves x iters x 65,536 flops);
+    out: float32 device tensor of at least blocks x 256 elements."""
+    if out.dtype.itemsize != 4 or out.numel() < blocks * 256:
+        raise ValueError("calibrate_mfma: out must hold blocks x 256 float32 values")
+    st = lib().mla_verify_calibrate_mfma(int(iters), int(blocks), _ptr(out), _stream(stream))
+    if st != OK:
+        raise MlaVerifyError(st, "mla_verify_calibrate_mfma")
+
+
+def calibrate_read(buf, blocks: int, out, stream=None) -> None:
+    """Enqueue the read stream over every byte of buf (a contiguous device
+    tensor); out: float32 device tensor of at least blocks x 256 elements."""
+    if not buf.is_contiguous():
+        raise ValueError("calibrate_read: buf must be contiguous")
+    if out.dtype.itemsize != 4 or out.numel() < blocks * 256:
+        raise ValueError("calibrate_read: out must hold blocks x 256 float32 values")
+    st = lib().mla_verify_calibrate_read(_ptr(buf), buf.numel() * buf.element_size(), int(blocks), _ptr(out),
+                                         _stream(stream))
+    if st != OK:
+        raise MlaVerifyError(st, "mla_verify_calibrate_read")
 
 
 def _stream(stream) -> int:

@@ -14,7 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libmla_verify.so")
 SOURCES = [os.path.join(PKG, "csrc", "mla_verify_api.cpp"),
-           os.path.join(PKG, "csrc", "mla_verify_kernels.hip")]
+           os.path.join(PKG, "csrc", "mla_verify_kernels.hip"),
+           os.path.join(PKG, "csrc", "mla_verify_calibrate.hip")]
 ARCH = "gfx950"
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared",

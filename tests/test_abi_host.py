@@ -179,6 +179,19 @@ def test_run_rejects_small_or_misaligned_workspace():
         B.ERR_INVALID_ARGUMENT
 
 
+def test_calibrate_mfma_rejects_bad_arguments_before_launch():
+    lib = B.lib()
+    assert lib.mla_verify_calibrate_mfma(0, 1, 1 << 44, None) == B.ERR_INVALID_ARGUMENT
+    assert lib.mla_verify_calibrate_mfma(1, 0, 1 << 44, None) == B.ERR_INVALID_ARGUMENT
+    assert lib.mla_verify_calibrate_mfma(1, 1, None, None) == B.ERR_INVALID_ARGUMENT
+    assert lib.mla_verify_calibrate_mfma(1, 1, (1 << 44) + 2, None) == B.ERR_INVALID_ARGUMENT
+    assert lib.mla_verify_calibrate_read(None, 1024, 1, 1 << 44, None) == B.ERR_INVALID_ARGUMENT
+    assert lib.mla_verify_calibrate_read(1 << 44, 1000, 1, 1 << 44, None) == B.ERR_INVALID_ARGUMENT
+    assert lib.mla_verify_calibrate_read((1 << 44) + 8, 1024, 1, 1 << 44, None) == B.ERR_INVALID_ARGUMENT
+    assert lib.mla_verify_calibrate_read(1 << 44, 1024, 0, 1 << 44, None) == B.ERR_INVALID_ARGUMENT
+    assert lib.mla_verify_calibrate_read(1 << 44, 1024, 1, None, None) == B.ERR_INVALID_ARGUMENT
+
+
 def test_status_strings():
     assert B.status_string(B.OK) == "ok"
     assert "workspace" in B.status_string(B.ERR_WORKSPACE_TOO_SMALL)
