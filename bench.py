@@ -276,19 +276,29 @@ def main():
     call_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
     ms_per_step = wall * 1e3 / args.steps
 
-    # cold calls: scrub the 256 MB Infinity Cache and L2 with a 1 GiB write first
-    cold_us = None
+    # cold calls: before each, push the call's data out of the 256 MB Infinity
+    # Cache and the L2s with a 1 GiB scrub, either read (clean lines: the call
+    # pays only for its misses; the reported cold figure) or written (the call
+    # also pays for writing back the dirty lines it evicts)
+    cold_us = cold_dirty_us = None
     if args.cold_calls > 0:
-        scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-        ce = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.cold_calls)]
-        for i in range(args.cold_calls):
-            scrub.fill_(float(i))
-            ce[i][0].record(stream)
-            step()
-            ce[i][1].record(stream)
-        torch.cuda.synchronize()
-        cold_us = float(np.median([e[0].elapsed_time(e[1]) for e in ce]) * 1e3)
-        del scrub
+        scrub = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        sums = torch.empty(4 * cus * 256, dtype=torch.float32, device="cuda")
+
+        def cold(scrub_fn):
+            ce = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.cold_calls)]
+            for i in range(args.cold_calls):
+                scrub_fn(i)
+                ce[i][0].record(stream)
+                step()
+                ce[i][1].record(stream)
+            torch.cuda.synchronize()
+            return float(np.median([e[0].elapsed_time(e[1]) for e in ce]) * 1e3)
+
+        cold_us = cold(lambda i: B.calibrate_read(scrub, 4 * cus, sums, sp))
+        cold_dirty_us = cold(lambda i: scrub.fill_(float(i)))
+        del scrub, sums
 
     # the same call with the fused KV save: the draft rows are handed over and
     # stored at out_cache_loc by the metadata launch (same values, so the pool
@@ -401,6 +411,7 @@ def main():
         "us_per_call": us_call,
         "us_per_call_each_p10_p50_p90": [float(np.percentile(call_ms, q) * 1e3) for q in (10, 50, 90)],
         "us_per_call_cold": cold_us,
+        "us_per_call_cold_after_write_scrub": cold_dirty_us,
         "kernel_us": {"meta": float(np.mean(meta_ms) * 1e3), "partial": part_us,
                       "merge": float(np.mean(merge_ms) * 1e3)},
         "tflops_per_call": flops / (us_call * 1e-6) / 1e12,
