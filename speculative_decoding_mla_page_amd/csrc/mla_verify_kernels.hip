@@ -992,8 +992,9 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
 #pragma unroll
           for (int dt = 0; dt < kDtPerWave; ++dt) vt[sv][dt] = v_operand(vslot, dt);
         }
-        // the tile loads of this iteration ride along with the MFMAs
-        if (rt == 1 && more_dma) {
+        // the tile loads of this iteration ride along with the MFMAs, right
+        // after the first row tile's, so their issue stalls come early
+        if (rt == 0 && more_dma) {
 #pragma unroll
           for (int k = 0; k < 4; ++k) issue_key(i + 2, next_slots, k);
         }
