@@ -4,7 +4,7 @@ matches a closed form of the operands the kernel builds."""
 import numpy as np
 import pytest
 
-from gpu_helpers import need_gpu, say
+from tests.gpu_helpers import need_gpu, say
 
 pytestmark = pytest.mark.gpu
 

@@ -4,7 +4,7 @@ gives bit-identical results."""
 import numpy as np
 import pytest
 
-from gpu_helpers import assert_gate, need_gpu, oracle, say
+from tests.gpu_helpers import assert_gate, need_gpu, oracle, say
 from workloads import gen
 
 pytestmark = pytest.mark.gpu

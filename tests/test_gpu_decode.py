@@ -3,7 +3,7 @@ the same boundary in its HBM-bound regime, checked against the oracle."""
 import numpy as np
 import pytest
 
-from gpu_helpers import assert_gate, need_gpu, oracle, run_gpu, say
+from tests.gpu_helpers import assert_gate, assert_rows_finite, need_gpu, oracle, oracle_blocked, run_gpu, say
 from workloads import gen
 
 pytestmark = pytest.mark.gpu
@@ -24,12 +24,18 @@ def test_decode_b32_h16_full():
     assert_gate(out, lse, ref_out, ref_lse, label="decode_b32_h16")
 
 
-def test_decode_b64_h128_sampled():
+def test_decode_b64_h128_full():
+    """64 requests x 1 node x 128 heads: every row against the oracle."""
     need_gpu()
+    from speculative_decoding_mla_page_amd import binding as B
     inst = gen.config("decode_b64_h128")
-    say("decode_b64_h128")
-    out, lse, v, _ = run_gpu(inst, max_tree_nodes=1)
+    say("decode_b64_h128 (all 64 tokens x 128 heads)")
+    out, lse, v, _ = run_gpu(inst, flags=B.FLAG_TRACE_KEYS, max_tree_nodes=1)
     assert v.error_word() == 0
-    tokens = [0, 17, 40, 63]
-    ref_out, ref_lse, _ = oracle(inst, tokens=tokens)
-    assert_gate(out, lse, ref_out, ref_lse, tokens=tokens, label="decode_b64_h128")
+    assert_rows_finite(out, lse, label="decode_b64_h128")
+    ref_out, ref_lse, rec = oracle_blocked(inst, block_tokens=16)
+    tr = v.region(v.layout.trace_offset, inst.total_kv + inst.total_q, __import__("torch").int64).cpu().numpy()
+    for b in range(inst.batch):
+        base = int(inst.kv_indptr[b]) + int(inst.qo_indptr[b])
+        assert np.array_equal(tr[base:base + len(rec["keys"][b])], rec["keys"][b]), f"request {b}"
+    assert_gate(out, lse, ref_out, ref_lse, label="decode_b64_h128")

@@ -5,7 +5,7 @@ bit for bit, the outputs against the oracle on the pool the rows belong in."""
 import numpy as np
 import pytest
 
-from gpu_helpers import assert_gate, need_gpu, oracle, say
+from tests.gpu_helpers import assert_gate, need_gpu, oracle, say
 from workloads import gen
 
 pytestmark = pytest.mark.gpu

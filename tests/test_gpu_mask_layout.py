@@ -6,7 +6,7 @@ import copy
 import numpy as np
 import pytest
 
-from gpu_helpers import assert_gate, need_gpu, oracle, run_gpu, say
+from tests.gpu_helpers import assert_gate, need_gpu, oracle, run_gpu, say
 from workloads import gen
 
 pytestmark = pytest.mark.gpu

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 from workloads import gen
-from tests.gpu_helpers import assert_gate, need_gpu, oracle, run_gpu, say
+from tests.gpu_helpers import assert_gate, assert_rows_finite, need_gpu, oracle, oracle_blocked, run_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -124,15 +124,18 @@ def test_small_tree_plans(max_nodes, prefixes, trees):
     assert_gate(out, lse, ref_out, ref_lse, label=f"max_tree_nodes={max_nodes}")
 
 
-def test_config_parity_h64_sampled():
-    """H = 64 (2,048 query rows): oracle on sampled tree nodes."""
+def test_config_parity_h64_full():
+    """H = 64 (2,048 query rows): every row against the oracle (computed four
+    tokens at a time), gathered keys and tree words bit-exact."""
     need_gpu()
+    from speculative_decoding_mla_page_amd import binding as B
     inst = gen.config("p91136_t32_h64")
-    say("config p91136_t32_h64")
-    out, lse, v, _ = run_gpu(inst)
-    tokens = [0, 5, 17, 31]
-    ref_out, ref_lse, _ = oracle(inst, tokens=tokens)
-    assert_gate(out, lse, ref_out, ref_lse, tokens=tokens, label="h64")
+    say("config p91136_t32_h64 (all 32 nodes x 64 heads)")
+    out, lse, v, _ = run_gpu(inst, flags=B.FLAG_TRACE_KEYS)
+    assert_rows_finite(out, lse, label="h64")
+    ref_out, ref_lse, rec = oracle_blocked(inst, block_tokens=4)
+    _check_metadata(inst, v, rec)
+    assert_gate(out, lse, ref_out, ref_lse, label="p91136_t32_h64")
 
 
 def test_mixed_batch_edges():
