@@ -1,6 +1,7 @@
 """Benchmark of tree-masked MLA verify attention on one MI355X.
 
-Workload (one step = one verify call = metadata build + split partials + merge):
+Workload (one step = one verify call = split partials, each workgroup planning
+from the raw metadata, + merge):
 1 request, 91,136-token prefix scattered over a 1,048,576-slot page_size=1 pool,
 32-node random draft tree, H = 8 heads, 576-wide bf16 latent (V = first 512
 dims), 1% of prefix rows scaled by 8, fp32 output + LSE.  Inputs are seeded
@@ -62,16 +63,24 @@ def kernel_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def algorithmic(inst):
-    """Algorithmic flops and KV bytes of one call: every query row (node x head)
-    takes 576 + 512 multiply-adds per visible-or-not key of its request."""
+def algorithmic(inst, kv_index_bytes=4, ocl_bytes=8):
+    """Algorithmic work of one call.  flops: every query row (node x head)
+    takes 576 + 512 multiply-adds per visible-or-not key of its request.
+    kv_bytes: the gathered latent rows (1,152 B per key).  bytes: everything
+    the call must move once - latent rows, prefix indices, tree slots, the
+    tree mask block, queries (1,152 B per row), out (2,048 B) and lse (4 B)
+    per row."""
     flops = 0
     kv_bytes = 0
+    all_bytes = 0
+    h = inst.num_heads
     for p, t in zip(inst.prefix_lens, inst.tree_sizes):
         n = p + t
-        flops += 2 * (t * inst.num_heads) * n * (576 + 512)
+        rows = t * h
+        flops += 2 * rows * n * (576 + 512)
         kv_bytes += n * 1152
-    return flops, kv_bytes
+        all_bytes += n * 1152 + p * kv_index_bytes + t * ocl_bytes + t * t + rows * 1152 + rows * (2048 + 4)
+    return flops, kv_bytes, all_bytes
 
 
 def read_traffic(workload: str):
@@ -217,7 +226,7 @@ def main():
         bench_graph(args)
         return
     inst = gen.config(workload)
-    flops, kv_bytes = algorithmic(inst)
+    flops, kv_bytes, alg_bytes = algorithmic(inst)
     di = DeviceInputs(inst)
     # the plan's tree-size bound is the largest draft tree the caller runs
     ver = Verifier.for_inputs(di, max_tree_nodes=max(1, max(int(t) for t in inst.tree_sizes)))
@@ -231,12 +240,10 @@ def main():
             B.run(ver.plan, a, ver.workspace, sp)
             return
         evs[0].record(stream)
-        B.run_phase(ver.plan, a, ver.workspace, B.PHASE_META, sp)
-        evs[1].record(stream)
         B.run_phase(ver.plan, a, ver.workspace, B.PHASE_PARTIAL, sp)
-        evs[2].record(stream)
+        evs[1].record(stream)
         B.run_phase(ver.plan, a, ver.workspace, B.PHASE_MERGE, sp)
-        evs[3].record(stream)
+        evs[2].record(stream)
 
     if args.calibration_copy_mib > 0:
         n = args.calibration_copy_mib << 18          # float32 elements
@@ -253,7 +260,7 @@ def main():
     if ver.error_word() != 0:
         raise RuntimeError(f"device error word {ver.error_word():#x}")
 
-    # timed region: K whole calls (mla_verify_run, three launches each) back to
+    # timed region: K whole calls (mla_verify_run, two launches each) back to
     # back on the stream, bracketed by one event pair and the host clock
     span = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
@@ -269,43 +276,50 @@ def main():
     # per-kernel times: the same K calls again, launched phase by phase with
     # events between the launches (the events add gaps, so this loop is not
     # the value; the partial kernel's mean here gives the roofline figure)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
-    meta_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    part_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    merge_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
-    call_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    part_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    merge_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    call_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
     ms_per_step = wall * 1e3 / args.steps
 
     # cold calls: before each, push the call's data out of the 256 MB Infinity
     # Cache and the L2s with a 1 GiB scrub, either read (clean lines: the call
-    # pays only for its misses; the reported cold figure) or written (the call
-    # also pays for writing back the dirty lines it evicts)
-    cold_us = cold_dirty_us = None
+    # pays only for its misses; the basis of the whole-call roofline fraction)
+    # or written (the call also pays for writing back the scrub's dirty lines
+    # it evicts); per-phase events give the partial kernel's cold duration
+    cold_us = cold_dirty_us = cold_part_us = None
     if args.cold_calls > 0:
         scrub = torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
         cus = torch.cuda.get_device_properties(0).multi_processor_count
         sums = torch.empty(4 * cus * 256, dtype=torch.float32, device="cuda")
 
-        def cold(scrub_fn):
-            ce = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.cold_calls)]
+        def cold(scrub_fn, phases=False):
+            ce = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.cold_calls)]
             for i in range(args.cold_calls):
                 scrub_fn(i)
-                ce[i][0].record(stream)
-                step()
-                ce[i][1].record(stream)
+                if phases:
+                    step(ce[i])
+                else:
+                    ce[i][0].record(stream)
+                    step()
+                    ce[i][2].record(stream)
             torch.cuda.synchronize()
-            return float(np.median([e[0].elapsed_time(e[1]) for e in ce]) * 1e3)
+            call = float(np.median([e[0].elapsed_time(e[2]) for e in ce]) * 1e3)
+            part = float(np.median([e[0].elapsed_time(e[1]) for e in ce]) * 1e3) if phases else None
+            return call, part
 
-        cold_us = cold(lambda i: B.calibrate_read(scrub, 4 * cus, sums, sp))
-        cold_dirty_us = cold(lambda i: scrub.fill_(float(i)))
+        read_scrub = lambda i: B.calibrate_read(scrub, 4 * cus, sums, sp)  # noqa: E731
+        cold_us, _ = cold(read_scrub)
+        _, cold_part_us = cold(read_scrub, phases=True)
+        cold_dirty_us, _ = cold(lambda i: scrub.fill_(float(i)))
         del scrub, sums
 
     # the same call with the fused KV save: the draft rows are handed over and
-    # stored at out_cache_loc by the metadata launch (same values, so the pool
-    # is unchanged); timed over its own loop, not the value
+    # stored at out_cache_loc by the split-partial launch (same values, so the
+    # pool is unchanged); timed over its own loop, not the value
     fused = None
     if args.fused_save_calls > 0:
         ocl = di.out_cache_loc[:di.total_q].to(torch.int64)
@@ -318,9 +332,8 @@ def main():
         fe = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.fused_save_calls)]
         for e in fe:
             e[0].record(stream)
-            B.run_phase(ver.plan, a2, ver.workspace, B.PHASE_META, sp)
-            e[1].record(stream)
             B.run_phase(ver.plan, a2, ver.workspace, B.PHASE_PARTIAL, sp)
+            e[1].record(stream)
             B.run_phase(ver.plan, a2, ver.workspace, B.PHASE_MERGE, sp)
         fe_all = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         fe_all[0].record(stream)
@@ -329,7 +342,7 @@ def main():
         fe_all[1].record(stream)
         torch.cuda.synchronize()
         fused = {"us_per_call": fe_all[0].elapsed_time(fe_all[1]) * 1e3 / args.fused_save_calls,
-                 "meta_us": float(np.median([e[0].elapsed_time(e[1]) for e in fe]) * 1e3),
+                 "partial_us": float(np.median([e[0].elapsed_time(e[1]) for e in fe]) * 1e3),
                  "rows_saved": int(di.total_q), "calls": args.fused_save_calls}
 
     # prefix compaction (KV defragmentation) onto fresh contiguous slots, then
@@ -375,24 +388,42 @@ def main():
     us_call = float(span_ms * 1e3 / args.steps)
     part_us = float(np.mean(part_ms) * 1e3)
     traffic = read_traffic(workload)
+    # the split-partial kernel's own algorithmic bytes: the call's less out and lse
+    rows_all = inst.total_q * inst.num_heads
+    part_bytes = alg_bytes - rows_all * (2048 + 4)
     # the bound of the partial kernel on this workload: MFMA when its flops take
-    # longer at peak than its KV bytes
+    # longer at peak than its bytes
     t_mfma = flops / (PEAK_MFMA_BF16_TFLOPS * 1e12)
-    t_hbm = kv_bytes / (PEAK_HBM_GBS * 1e9)
-    if t_mfma >= t_hbm:
-        achieved = flops / (part_us * 1e-6) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_MFMA_BF16_TFLOPS}
+    if flops / (PEAK_MFMA_BF16_TFLOPS * 1e12) >= part_bytes / (PEAK_HBM_GBS * 1e9):
+        work, scale, peak, unit, bound = flops, 1e12, PEAK_MFMA_BF16_TFLOPS, "TFLOP/s", "mfma"
     else:
-        achieved = kv_bytes / (part_us * 1e-6) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS}
-    roof.update({"traffic": traffic, "kernel": "partial_kernel", "kernel_source_sha256_16": kernel_hash()})
+        work, scale, peak, unit, bound = part_bytes, 1e9, PEAK_HBM_GBS, "GB/s", "hbm"
+    achieved = work / (part_us * 1e-6) / scale
+    roof = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+            "traffic": traffic, "kernel": "partial_kernel", "kernel_source_sha256_16": kernel_hash(),
+            "algorithmic_per_launch": work, "launch_us_warm": part_us}
+    if cold_part_us:
+        roof["launch_us_cold"] = cold_part_us
+        roof["frac_cold"] = work / (cold_part_us * 1e-6) / scale / peak
+    if bound == "mfma":
+        # the split P (hi + lo) runs 2 x (576 + 512 + 512) = 3,200 MFMA flops per
+        # (row, key) for 2,176 algorithmic ones: the design's ceiling on frac
+        roof["design_ceiling_frac"] = 2176.0 / 3200.0
+    # the whole call against its roofline: all algorithmic bytes vs flops, over
+    # the cold (read-scrubbed) call; the warm and write-scrubbed calls beside
+    t_hbm = alg_bytes / (PEAK_HBM_GBS * 1e9)
+    t_roof = max(t_hbm, t_mfma)
+    call_basis = cold_us if cold_us else us_call
+    roof_call = {"t_roof_us": t_roof * 1e6, "basis": "cold (read-scrubbed) call" if cold_us else "warm call",
+                 "frac": t_roof / (call_basis * 1e-6), "frac_hbm": t_hbm / (call_basis * 1e-6),
+                 "frac_mfma": t_mfma / (call_basis * 1e-6), "frac_warm": t_roof / (us_call * 1e-6)}
+    if cold_dirty_us:
+        roof_call["frac_after_write_scrub"] = t_roof / (cold_dirty_us * 1e-6)
     achievable = None
     if not args.no_achievable:
         peaks = achievable_peaks(torch, B)
-        t_roof_a = max(kv_bytes / (peaks["hbm_read_GBps"] * 1e9), flops / (peaks["mfma_bf16_TFLOPs"] * 1e12))
-        achievable = with_achievable(peaks, roof["bound"], achieved, t_roof_a, us_call * 1e-6)
+        t_roof_a = max(alg_bytes / (peaks["hbm_read_GBps"] * 1e9), flops / (peaks["mfma_bf16_TFLOPs"] * 1e12))
+        achievable = with_achievable(peaks, bound, achieved, t_roof_a, call_basis * 1e-6)
     metric = METRIC if workload == WORKLOAD else f"µs/call + effective KV GB/s & %roofline, {workload}"
     result = {
         "metric": metric,
@@ -415,13 +446,11 @@ def main():
         "us_per_call_each_p10_p50_p90": [float(np.percentile(call_ms, q) * 1e3) for q in (10, 50, 90)],
         "us_per_call_cold": cold_us,
         "us_per_call_cold_after_write_scrub": cold_dirty_us,
-        "kernel_us": {"meta": float(np.mean(meta_ms) * 1e3), "partial": part_us,
-                      "merge": float(np.mean(merge_ms) * 1e3)},
+        "kernel_us": {"partial": part_us, "merge": float(np.mean(merge_ms) * 1e3)},
         "tflops_per_call": flops / (us_call * 1e-6) / 1e12,
-        "algorithmic": {"flops": flops, "kv_bytes": kv_bytes},
+        "algorithmic": {"flops": flops, "kv_bytes": kv_bytes, "bytes": alg_bytes},
         "roofline": roof,
-        "roofline_call": {"t_roof_us": max(t_hbm, t_mfma) * 1e6, "frac": max(t_hbm, t_mfma) / (us_call * 1e-6),
-                          "frac_hbm": t_hbm / (us_call * 1e-6), "frac_mfma": t_mfma / (us_call * 1e-6)},
+        "roofline_call": roof_call,
         "achievable": achievable,
         "fused_kv_save": fused,
         "compaction": compaction,
@@ -480,9 +509,8 @@ def bench_graph(args):
                              ("mask_indptr", rep.mask_indptr), ("kv_indices", rep.kv_indices),
                              ("out_cache_loc", rep.out_cache_loc), ("custom_mask", rep.custom_mask))}
         host["q"] = torch.from_numpy(rep.q.view(np.int16))
-        flops = sum(2 * t * h * (pp + t) * (576 + 512) for pp, t in zip(rep.prefix_lens, rep.tree_sizes))
-        kv_bytes = (rep.total_kv + rep.total_q) * 1152
-        draws.append((host, flops, kv_bytes))
+        flops, kv_bytes, all_bytes = algorithmic(rep)
+        draws.append((host, flops, kv_bytes, all_bytes))
 
     def fill(st, host):
         for k, t in host.items():
@@ -515,7 +543,7 @@ def bench_graph(args):
 
     def replay(i, evs=None):
         k = i % 2
-        host, _, _ = draws[i % n_draws]
+        host = draws[i % n_draws][0]
         with torch.cuda.stream(copy_stream):
             copy_stream.wait_event(done[k])       # replay i - 2 has finished with set k
             fill(sets[k], host)                   # returns once the copies are done
@@ -533,28 +561,29 @@ def bench_graph(args):
     if ver.error_word() != 0:
         raise RuntimeError(f"device error word {ver.error_word():#x}")
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    flops_all = bytes_all = 0
+    flops_all = bytes_all = alg_all = 0
     t0 = time.perf_counter()
     for i in range(args.steps):
         replay(args.warmup + i, evs[i])
-        _, fl, kb = draws[(args.warmup + i) % n_draws]
+        _, fl, kb, ab = draws[(args.warmup + i) % n_draws]
         flops_all += fl
         bytes_all += kb
+        alg_all += ab
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     if ver.error_word() != 0:
         raise RuntimeError(f"device error word {ver.error_word():#x}")
     rep_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     total_s = float(rep_ms.sum()) * 1e-3
-    t_hbm = bytes_all / (PEAK_HBM_GBS * 1e9)
+    t_hbm = alg_all / (PEAK_HBM_GBS * 1e9)
     t_mfma = flops_all / (PEAK_MFMA_BF16_TFLOPS * 1e12)
     bound = "mfma" if t_mfma >= t_hbm else "hbm"
-    achieved = (flops_all / total_s / 1e12) if bound == "mfma" else (bytes_all / total_s / 1e9)
+    achieved = (flops_all / total_s / 1e12) if bound == "mfma" else (alg_all / total_s / 1e9)
     peak = PEAK_MFMA_BF16_TFLOPS if bound == "mfma" else PEAK_HBM_GBS
     achievable = None
     if not args.no_achievable:
         peaks = achievable_peaks(torch, B)
-        t_roof_a = max(bytes_all / (peaks["hbm_read_GBps"] * 1e9), flops_all / (peaks["mfma_bf16_TFLOPs"] * 1e12))
+        t_roof_a = max(alg_all / (peaks["hbm_read_GBps"] * 1e9), flops_all / (peaks["mfma_bf16_TFLOPs"] * 1e12))
         achievable = with_achievable(peaks, bound, achieved, t_roof_a, total_s)
     result = {
         "metric": f"µs/call + effective KV GB/s & %roofline, {GRAPH_WORKLOAD}",
@@ -575,10 +604,11 @@ def bench_graph(args):
         "us_per_call": float(rep_ms.mean() * 1e3),
         "us_per_call_each_p10_p50_p90": [float(np.percentile(rep_ms, q) * 1e3) for q in (10, 50, 90)],
         "tflops_per_call": flops_all / total_s / 1e12,
-        "algorithmic": {"flops_per_call": flops_all / args.steps, "kv_bytes_per_call": bytes_all / args.steps},
+        "algorithmic": {"flops_per_call": flops_all / args.steps, "kv_bytes_per_call": bytes_all / args.steps,
+                        "bytes_per_call": alg_all / args.steps},
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s" if bound == "mfma" else "GB/s", "frac": achieved / peak,
-                     "traffic": None, "kernel": "whole call (graph replay: metadata, partial, merge)"},
+                     "traffic": None, "kernel": "whole call (graph replay: split partials with the device-side plan, merge)"},
         "roofline_call": {"frac": max(t_hbm, t_mfma) / total_s, "frac_hbm": t_hbm / total_s,
                           "frac_mfma": t_mfma / total_s},
         "achievable": achievable,

@@ -32,8 +32,9 @@
  * Errors: every entry point returns a status and checks host-visible arguments
  * only.  Problems found on the device (inconsistent indptrs, a tree larger than
  * the plan allows, a slot outside the pool) set bits of the error word at the
- * start of the workspace (mla_verify_layout_t.header_offset) and the affected
- * output rows are written as NaN; the caller reads the word after its own sync.
+ * start of the workspace (mla_verify_layout_t.header_offset, complete once the
+ * call has run) and the affected output rows are written as NaN; the caller
+ * reads the word after its own sync.
  */
 #ifndef MLA_VERIFY_H_
 #define MLA_VERIFY_H_
@@ -45,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MLA_VERIFY_ABI_VERSION 6
+#define MLA_VERIFY_ABI_VERSION 7
 #define MLA_VERIFY_D_QK 576          /* latent width used by Q.K^T (512 + 64 rope) */
 #define MLA_VERIFY_D_V 512           /* V = latent dims [0, 512) */
 #define MLA_VERIFY_MAX_TREE_NODES 64 /* tree visibility is packed into one 64-bit word */
@@ -123,9 +124,10 @@ typedef struct {
  *                 16-byte aligned, strides multiples of 8.
  *   kv_pool       bf16 [num_slots, kv_row_stride], kv_row_stride >= 576 and a
  *                 multiple of 8, 16-byte aligned; num_slots < 2^31 and
- *                 kv_row_stride < 2^30 (MLA_VERIFY_ERR_UNSUPPORTED otherwise).  page_size = 1: slot s is
- *                 one token's 576-wide latent row.  The rows of this call's
- *                 draft tokens must already be stored at out_cache_loc.
+ *                 kv_row_stride < 2^30 (MLA_VERIFY_ERR_UNSUPPORTED otherwise).
+ *                 page_size = 1: slot s is one token's 576-wide latent row.
+ *                 Without kv_new the rows of this call's draft tokens must
+ *                 already be stored at out_cache_loc.
  *   qo_indptr     int32 [B+1], qo_indptr[0] = 0: request b owns query tokens
  *                 [qo_indptr[b], qo_indptr[b+1]), T_b of them, its tree nodes
  *                 in node order.
@@ -145,12 +147,13 @@ typedef struct {
  *   kv_new        bf16 [sum T, >= 576] at kv_new + t*kv_new_stride_tok, or NULL.
  *                 When given, the call first stores row t (576 values) into
  *                 the pool at slot out_cache_loc[t] (the KV save of this
- *                 step's draft tokens, fused into the metadata launch), so the
- *                 pool must be writable and those slots distinct; rows whose
- *                 slot lies outside the pool are not stored (the slot range
- *                 error is raised as for any gathered slot).  16-byte aligned,
- *                 stride a multiple of 8.  When NULL the rows must already be
- *                 in the pool.
+ *                 step's draft tokens, fused into the call), then attends over
+ *                 it, so the pool must be writable and those slots distinct
+ *                 and fresh: none of them may appear in this call's
+ *                 kv_indices.  Rows whose slot lies outside the pool are not
+ *                 stored (the slot range error is raised as for any gathered
+ *                 slot); with a metadata error nothing is stored.  16-byte
+ *                 aligned, stride a multiple of 8.
  * A row that sees no key (P_b = 0 and an all-zero mask row) gets out = 0 and
  * lse = -inf.  Key order within a request is the prefix, then the tree nodes;
  * a slot listed twice is two keys.  Scores are sm_scale * (q . k).
@@ -184,49 +187,59 @@ typedef struct {
 typedef struct {
   uint64_t total_bytes;
   uint64_t header_offset;     /* uint32 error word, int32 n_items, int32 total_q, int32 chunk_keys, int32 batch,
-                                 int32 max_chunks (key ranges of the request with the most) */
+                                 int32 max_chunks (key ranges of the request with the most), uint32 metadata
+                                 error bits */
   uint64_t request_offset;    /* int32 [max_batch][8]: P, T, q0, kv0, row_blocks, chunks, item_base, mask0 */
   uint64_t anc_offset;        /* uint64 [max_q_tokens]: packed tree visibility of each node */
   uint64_t items_offset;      /* int32 [item_capacity][8]: b, row_block, chunk, key0, key1, row0, nrows, 0 */
   uint64_t partial_o_offset;  /* fp32 [item_capacity][rows_per_item][512] unnormalised partial outputs */
   uint64_t partial_ml_offset; /* fp32 [item_capacity][rows_per_item][2] running max (log2 units) and sum */
-  uint64_t trace_offset;      /* int64 [max_kv_tokens + max_q_tokens] gathered slots; 0 without the trace flag */
-  uint64_t slots_offset;      /* int32 [max_kv_tokens + max_q_tokens] each request's keys (prefix then tree)
-                                 at kv_indptr[b] + qo_indptr[b] + j: the pool slot, -1 outside the pool,
-                                 -2 for a prefix key a checked full-row mask hides */
+  uint64_t trace_offset;      /* int64 [max_kv_tokens + max_q_tokens]: request b's key j at
+                                 kv_indptr[b] + qo_indptr[b] + j, the index value it was gathered by;
+                                 0 without the trace flag */
   uint64_t stats_offset;      /* mla_verify_compare_stats_t written by mla_verify_compare */
   uint64_t tokens_offset;     /* int32 [max_q_tokens][4]: per query token, its request's first token,
                                  first work item, row blocks and key ranges (read by the merge) */
-  uint64_t launch_offset;     /* int32 [partial_grid][8]: per split-partial workgroup, its item (-1: none),
-                                 key0, key1, row0, nrows, and its request's P, q0, kv0 + q0 */
+  uint64_t errors_offset;     /* int32 [partial_grid]: device error bits found by each split-partial
+                                 workgroup (folded into the error word by the merge) */
   int32_t item_capacity;
   int32_t rows_per_item;      /* query rows (token x head) per work item */
   int32_t keys_per_tile;      /* keys staged per inner-loop step */
   int32_t target_items;
   int32_t partial_grid;       /* workgroups of the split-partial launch */
   int32_t merge_grid;         /* workgroups of the merge launch */
-  int32_t meta_grid;          /* workgroups of the metadata launch (1 + slot-staging workgroups) */
-  int32_t reserved;
 } mla_verify_layout_t;
 
-/* Validate a config and compute the plan (host arithmetic; the only possible
-   HIP call is the compute-unit query when cfg->cu_count == 0). */
+/* Validate a config and compute the plan: host arithmetic only (the one
+   possible HIP call is the compute-unit query when cfg->cu_count == 0).  The
+   plan fixes both launch grids, so that a captured call stays valid while the
+   buffers' contents change between replays ("The Capture-Safe Kernel",
+   Decision 3: a fixed split grid; Decision 6: buffers refreshed in place). */
 mla_verify_status_t mla_verify_plan(const mla_verify_config_t* cfg, mla_verify_plan_t* plan);
 
-/* Bytes of device workspace run() needs for this plan (256-byte aligned base). */
+/* Bytes of device workspace run() needs for this plan (256-byte aligned
+   base).  The workspace holds the partial softmax statistics of the key
+   ranges and the plan tables; the caller allocates it once and passes it to
+   every call, so no call allocates ("The Capture-Safe Kernel", Decision 4). */
 mla_verify_status_t mla_verify_workspace_size(const mla_verify_plan_t* plan, size_t* bytes);
 
 /* Enqueue the verify attention on `stream` (a hipStream_t; NULL = the null
-   stream): three kernel launches (metadata build, split partials, merge) and
-   nothing else.  Capture-safe.  workspace: device memory of at least
-   workspace_size bytes, 256-byte aligned, owned by the caller; its previous
-   contents are ignored. */
+   stream): two kernel launches and nothing else - split partials (each
+   workgroup derives the plan, prefix lengths and tree words from the raw
+   metadata buffers on the device: "The Capture-Safe Kernel", Decisions 1, 2
+   and 5) and the merge of the partial statistics (Decision 4).  It makes no
+   allocation, host sync, host read of device data or temporary, so it may be
+   recorded into a hipGraph ("The Capture-Safe Kernel", The Core Problem).
+   workspace: device memory of at least workspace_size bytes, 256-byte
+   aligned, owned by the caller; its previous contents are ignored.  Returns
+   the first argument error found (nothing is enqueued then) or
+   MLA_VERIFY_ERR_LAUNCH if HIP refuses a launch. */
 mla_verify_status_t mla_verify_run(const mla_verify_plan_t* plan, const mla_verify_args_t* args,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
-/* One of run()'s three launches (phase 0 = metadata build, 1 = split partials,
-   2 = merge), with the same checks; run() == phases 0, 1, 2 in order on one
-   stream.  For per-kernel timing. */
+/* One of run()'s two launches (phase 0 = split partials with the device-side
+   plan, 1 = merge), with the same checks; run() == phases 0, 1 in order on
+   one stream.  For per-kernel timing. */
 mla_verify_status_t mla_verify_run_phase(const mla_verify_plan_t* plan, const mla_verify_args_t* args,
                                          void* workspace, size_t workspace_bytes, void* stream,
                                          int32_t phase);
@@ -239,9 +252,10 @@ mla_verify_status_t mla_verify_workspace_layout(const mla_verify_plan_t* plan,
 const char* mla_verify_status_string(mla_verify_status_t status);
 
 /*
- * Shadow comparison (the pages' "validate" mode: the serving system keeps
- * returning its own attention result while this library's result is computed
- * beside it and compared).  After run() on the same stream, compare() checks
+ * Shadow comparison ("The Launch Wrapper", The Design Decision: Three Modes of
+ * Operation - the validate mode: the serving system keeps returning its own
+ * attention result while this library's result is computed beside it and
+ * compared).  After run() on the same stream, compare() checks
  * args->out / args->lse against the caller's reference, in the same layout,
  * over the call's query tokens, and accumulates into the workspace's stats
  * region (zeroed by every run()); read it after a sync.  One launch,
@@ -266,7 +280,10 @@ mla_verify_status_t mla_verify_compare(const mla_verify_plan_t* plan, const mla_
                                        size_t workspace_bytes, void* stream);
 
 /*
- * Prefix compaction (KV defragmentation): request b's prefix rows (the slots
+ * Prefix compaction (KV defragmentation, the later phase planned in "The
+ * Integration Chasm", The Decision: Adapt the Kernel, Not the System, and "The
+ * Capture-Safe Kernel", The Context: A Long Road to Production; the pages give
+ * no algorithm, this is the plainest one): request b's prefix rows (the slots
  * kv_indices[kv_indptr[b] + j], j < P_b) are copied to the contiguous slots
  * dst_start[b] + j, and those kv_indices entries are rewritten to the new
  * slots, in place.  Uses batch_size, kv_pool (writable), kv_row_stride,

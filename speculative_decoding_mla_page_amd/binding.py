@@ -36,7 +36,8 @@ DEVERR_SLOT_RANGE = 1 << 4
 DEVERR_CAPACITY = 1 << 5
 DEVERR_MASK_PREFIX = 1 << 6
 
-PHASE_META, PHASE_PARTIAL, PHASE_MERGE = 0, 1, 2
+PHASE_PARTIAL, PHASE_MERGE = 0, 1
+ABI_VERSION = 7
 
 
 class Config(ctypes.Structure):
@@ -95,18 +96,15 @@ class Layout(ctypes.Structure):
         ("partial_o_offset", ctypes.c_uint64),
         ("partial_ml_offset", ctypes.c_uint64),
         ("trace_offset", ctypes.c_uint64),
-        ("slots_offset", ctypes.c_uint64),
         ("stats_offset", ctypes.c_uint64),
         ("tokens_offset", ctypes.c_uint64),
-        ("launch_offset", ctypes.c_uint64),
+        ("errors_offset", ctypes.c_uint64),
         ("item_capacity", ctypes.c_int32),
         ("rows_per_item", ctypes.c_int32),
         ("keys_per_tile", ctypes.c_int32),
         ("target_items", ctypes.c_int32),
         ("partial_grid", ctypes.c_int32),
         ("merge_grid", ctypes.c_int32),
-        ("meta_grid", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -305,7 +303,7 @@ def _stream(stream) -> int:
 
 
 def run(p: Plan, args: Args, workspace, stream=None) -> None:
-    """Enqueue the three launches on `stream` (default: torch's current stream)."""
+    """Enqueue the two launches on `stream` (default: torch's current stream)."""
     st = lib().mla_verify_run(ctypes.byref(p), ctypes.byref(args), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _stream(stream))
     if st != OK:

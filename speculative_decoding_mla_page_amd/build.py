@@ -27,7 +27,7 @@ FLAGS = [
     # is rescaled in place, and the AGPR form makes the compiler copy it
     # between register files on every key tile
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
-    # workgroup-wide counters (the metadata kernel's per-request sums) reduce
+    # workgroup-wide counters (the device-side planner's per-request sums) reduce
     # each wave in DPP steps before its one atomic, instead of a scalar loop
     # over the active lanes
     "-mllvm", "-amdgpu-atomic-optimizer-strategy=DPP",

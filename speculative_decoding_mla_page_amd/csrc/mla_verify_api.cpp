@@ -1,8 +1,10 @@
 // Host side of the C-ABI: plan arithmetic, workspace layout, argument checks
-// and the three launches of a call.  Owns no device memory and keeps no state.
+// and the two launches of a call.  Owns no device memory and keeps no state.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <string.h>
+
+#include <algorithm>
 
 #include "mla_verify_internal.h"
 
@@ -39,7 +41,7 @@ mla_verify_status_t check_args(const PlanImpl& pl, const mla_verify_args_t* a, c
   if (!aligned(a->kv_pool, 16) || a->kv_row_stride < kDqk || a->kv_row_stride % 8 ||
       a->num_slots <= 0)
     return MLA_VERIFY_ERR_INVALID_ARGUMENT;
-  // slots are staged as int32 and row offsets formed as 32-bit x 32-bit products
+  // slots are carried as int32 and row offsets formed as 32-bit x 32-bit products
   if (a->num_slots > INT32_MAX || a->kv_row_stride > (INT32_MAX >> 1)) return MLA_VERIFY_ERR_UNSUPPORTED;
   if (!aligned(a->out, 16) || a->out_stride_tok <= 0 || a->out_stride_head <= 0 ||
       a->out_stride_tok % 4 || a->out_stride_head % 4)
@@ -47,8 +49,10 @@ mla_verify_status_t check_args(const PlanImpl& pl, const mla_verify_args_t* a, c
   if (a->lse && (!aligned(a->lse, 4) || a->lse_stride_tok <= 0))
     return MLA_VERIFY_ERR_INVALID_ARGUMENT;
   // 16-byte row copies of the draft rows into the pool
-  if (a->kv_new && (!aligned(a->kv_new, 16) || a->kv_new_stride_tok < kDqk || a->kv_new_stride_tok % 8))
+  if (a->kv_new && (!aligned(a->kv_new, 16) || a->kv_new_stride_tok < kDqk || a->kv_new_stride_tok % 8 ||
+                    a->kv_new_stride_tok > (INT32_MAX >> 1)))
     return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+
   if (!aligned(a->qo_indptr, 4) || !aligned(a->kv_indptr, 4) || !aligned(a->mask_indptr, 4))
     return MLA_VERIFY_ERR_INVALID_ARGUMENT;
   if (!aligned(a->kv_indices, c.kv_indices_dtype == MLA_VERIFY_I64 ? 8 : 4) ||
@@ -101,10 +105,9 @@ KernelParams make_params(const PlanImpl& pl, const mla_verify_args_t* a, void* w
   p.items = reinterpret_cast<int32_t*>(base + l.items_offset);
   p.part_o = reinterpret_cast<float*>(base + l.partial_o_offset);
   p.part_ml = reinterpret_cast<float*>(base + l.partial_ml_offset);
-  p.slots = reinterpret_cast<int32_t*>(base + l.slots_offset);
   p.stats = reinterpret_cast<mla_verify_compare_stats_t*>(base + l.stats_offset);
   p.tok = reinterpret_cast<int32_t*>(base + l.tokens_offset);
-  p.launch = reinterpret_cast<int32_t*>(base + l.launch_offset);
+  p.errs = reinterpret_cast<int32_t*>(base + l.errors_offset);
   p.partial_grid = l.partial_grid;
   p.trace = (c.flags & MLA_VERIFY_FLAG_TRACE_KEYS) ? reinterpret_cast<int64_t*>(base + l.trace_offset)
                                                    : nullptr;
@@ -171,7 +174,7 @@ mla_verify_status_t mla_verify_plan(const mla_verify_config_t* cfg, mla_verify_p
   mla_verify_layout_t& l = impl.layout;
   // every request adds at most one partly filled key range per row block
   const int64_t row_blocks_bound = (max_rows + kRowsPerItem - 1) / kRowsPerItem + c.max_batch;
-  // room for two rounds of target items (the metadata kernel may choose
+  // room for two rounds of target items (the device-side plan may choose
   // shorter key ranges over two rounds when many short requests would leave
   // one round badly balanced), plus the partly filled ranges
   const int64_t capacity = 2 * (int64_t)target + row_blocks_bound;
@@ -180,15 +183,13 @@ mla_verify_status_t mla_verify_plan(const mla_verify_config_t* cfg, mla_verify_p
   l.rows_per_item = kRowsPerItem;
   l.keys_per_tile = kKeysPerTile;
   l.target_items = target;
-  // the partial kernel maps workgroups to items XCD by XCD (8 XCDs): whole groups of 8
-  l.partial_grid = (int32_t)((capacity + 7) / 8 * 8);
+  // the split-partial launch: about one workgroup per target item (one per
+  // compute unit), whole groups of 8 (one per XCD), enough that none runs
+  // more than kMaxItemsPerWg items
+  const int64_t per_xcd_max = (capacity + 7) / 8;
+  const int64_t g8 = std::max<int64_t>((target + 7) / 8, (per_xcd_max + kMaxItemsPerWg - 1) / kMaxItemsPerWg);
+  l.partial_grid = (int32_t)(8 * g8);
   l.merge_grid = (int32_t)max_rows;
-  // slot staging: one workgroup per kMetaKeysPerGroup keys of capacity, at most kMetaStageGroups
-  const int64_t stage_keys = (int64_t)c.max_kv_tokens + c.max_q_tokens;
-  int64_t stage = (stage_keys + kMetaKeysPerGroup - 1) / kMetaKeysPerGroup;
-  if (stage > kMetaStageGroups) stage = kMetaStageGroups;
-  if (stage < 1) stage = 1;
-  l.meta_grid = (int32_t)(1 + stage);
 
   uint64_t off = 0;
   l.header_offset = off;
@@ -208,14 +209,12 @@ mla_verify_status_t mla_verify_plan(const mla_verify_config_t* cfg, mla_verify_p
     l.trace_offset = off;
     off = align_up(off + ((uint64_t)c.max_kv_tokens + c.max_q_tokens) * sizeof(int64_t));
   }
-  l.slots_offset = off;
-  off = align_up(off + ((uint64_t)c.max_kv_tokens + c.max_q_tokens) * sizeof(int32_t));
   l.stats_offset = off;
   off = align_up(off + sizeof(mla_verify_compare_stats_t));
   l.tokens_offset = off;
   off = align_up(off + (uint64_t)c.max_q_tokens * 4 * sizeof(int32_t));
-  l.launch_offset = off;
-  off = align_up(off + (uint64_t)l.partial_grid * 8 * sizeof(int32_t));
+  l.errors_offset = off;
+  off = align_up(off + (uint64_t)l.partial_grid * sizeof(int32_t));
   l.total_bytes = off;
 
   memset(plan, 0, sizeof(*plan));
@@ -245,14 +244,11 @@ mla_verify_status_t mla_verify_run_phase(const mla_verify_plan_t* plan, const ml
                                          int32_t phase) {
   const PlanImpl* pl = as_impl(plan);
   if (!pl) return MLA_VERIFY_ERR_BAD_PLAN;
-  if (phase < 0 || phase > 2) return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  if (phase < 0 || phase > 1) return MLA_VERIFY_ERR_INVALID_ARGUMENT;
   const mla_verify_status_t st = check_args(*pl, args, workspace, workspace_bytes);
   if (st != MLA_VERIFY_OK) return st;
   const KernelParams p = make_params(*pl, args, workspace);
-  int rc = 0;
-  if (phase == 0) rc = launch_meta(p, pl->layout, stream);
-  else if (phase == 1) rc = launch_partial(p, pl->layout, stream);
-  else rc = launch_merge(p, pl->layout, stream);
+  const int rc = phase == 0 ? launch_partial(p, pl->layout, stream) : launch_merge(p, pl->layout, stream);
   return rc == 0 ? MLA_VERIFY_OK : MLA_VERIFY_ERR_LAUNCH;
 }
 
@@ -313,7 +309,6 @@ mla_verify_status_t mla_verify_run(const mla_verify_plan_t* plan, const mla_veri
   const mla_verify_status_t st = check_args(*pl, args, workspace, workspace_bytes);
   if (st != MLA_VERIFY_OK) return st;
   const KernelParams p = make_params(*pl, args, workspace);
-  if (launch_meta(p, pl->layout, stream) != 0) return MLA_VERIFY_ERR_LAUNCH;
   if (launch_partial(p, pl->layout, stream) != 0) return MLA_VERIFY_ERR_LAUNCH;
   if (launch_merge(p, pl->layout, stream) != 0) return MLA_VERIFY_ERR_LAUNCH;
   return MLA_VERIFY_OK;

@@ -18,12 +18,10 @@ constexpr int kStages = 3;                 // LDS slots of key tiles (V part)
 constexpr int kIdxKeys = 256;              // slots staged per index block (8 tiles)
 constexpr int kPVWaves = 8;                // PV waves per workgroup (64 output dims each)
 constexpr int kPartialThreads = (kWaves + kPVWaves) * 64;   // score waves + PV waves
-constexpr int kMetaThreads = 256;
-constexpr int kMetaKeysPerGroup = 1024;    // slot-staging workgroups: one per this many keys of capacity
-constexpr int kMetaStageGroups = 256;      // ... and at most this many
 constexpr int kMergeThreads = 512;         // 8 waves per output row, each lane 8 of the 512 dims
 constexpr int kMinChunkKeys = 128;         // shortest key range of a work item
-constexpr int kMaxBatch = 1024;            // per-request tables live in LDS of the metadata kernel
+constexpr int kMaxItemsPerWg = 4;          // work items one split-partial workgroup runs, at most
+constexpr int kMaxBatch = 1024;            // per-request plan tables live in LDS of every split-partial workgroup
 constexpr uint32_t kPlanMagic = 0x5641'4c4du;  // "MLAV"
 
 // request table columns (int32 x 8 per request)
@@ -32,19 +30,22 @@ enum { RQ_P = 0, RQ_T, RQ_Q0, RQ_KV0, RQ_RB, RQ_CHUNKS, RQ_ITEM0, RQ_MASK0 };
 enum { IT_B = 0, IT_RB, IT_CHUNK, IT_KEY0, IT_KEY1, IT_ROW0, IT_NROWS };
 
 struct WsHeader {
-  uint32_t err;
+  uint32_t err;         // every device error bit of the call (written by the merge launch)
   int32_t n_items;
   int32_t total_q;
   int32_t chunk_keys;
   int32_t batch;
   int32_t max_chunks;   // key ranges of the request with the most
-  int32_t pad[2];
+  uint32_t err_meta;    // the metadata checks' bits alone (written by the split-partial launch)
+  int32_t pad;
 };
 
 constexpr uint32_t kMetaErrMask = MLA_VERIFY_DEVERR_QO_INDPTR | MLA_VERIFY_DEVERR_KV_INDPTR |
                                   MLA_VERIFY_DEVERR_TREE_SIZE | MLA_VERIFY_DEVERR_MASK_INDPTR |
                                   MLA_VERIFY_DEVERR_CAPACITY;
-constexpr int32_t kSlotMaskedPrefix = -2;   // staged slot of a prefix key a checked full-row mask hides
+// a key's slot as the split-partial kernel carries it: >= 0 a pool slot; a
+// slot outside the pool is kSlotBad (the item is poisoned and reads slot 0)
+constexpr int32_t kSlotBad = -1;
 
 struct PlanImpl {
   uint32_t magic;
@@ -77,7 +78,7 @@ struct KernelParams {
   int64_t out_stride_head;
   float* lse;
   int64_t lse_stride_tok;
-  const uint16_t* kv_new;       // optional draft rows stored into the pool by the metadata launch
+  const uint16_t* kv_new;       // optional draft rows, stored into the pool before they are gathered
   int64_t kv_new_stride_tok;
   // plan
   int32_t kv_idx64;
@@ -93,13 +94,12 @@ struct KernelParams {
   int32_t* req;
   uint64_t* anc;
   int32_t* tok;   // [max_q_tokens][4]: request's first token, first item, row blocks, key ranges
-  int32_t* launch;   // [partial_grid][8]: item (-1: none), key0, key1, row0, nrows, P, q0, slot base
+  int32_t* errs;  // [partial_grid]: device error bits found by each split-partial workgroup
   int32_t partial_grid;
   int32_t* items;
   float* part_o;
   float* part_ml;
   int64_t* trace;
-  int32_t* slots;
   mla_verify_compare_stats_t* stats;
   // shadow comparison only
   const float* ref_out;
@@ -109,7 +109,6 @@ struct KernelParams {
   int64_t ref_lse_stride_tok;
 };
 
-int launch_meta(const KernelParams& p, const mla_verify_layout_t& lay, void* stream);
 int launch_partial(const KernelParams& p, const mla_verify_layout_t& lay, void* stream);
 int launch_merge(const KernelParams& p, const mla_verify_layout_t& lay, void* stream);
 int launch_compare(const KernelParams& p, const mla_verify_layout_t& lay, void* stream);

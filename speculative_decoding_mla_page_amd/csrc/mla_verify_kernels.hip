@@ -1,25 +1,26 @@
-// gfx950 kernels of tree-masked MLA verify attention.
+// gfx950 kernels of tree-masked MLA verify attention: a call is two launches.
 //
-//   meta_kernel     per-request lengths and validation, packed tree-visibility
-//                   words, and the table of (request, row block, key range)
-//                   work items, all derived on the device from the serving
-//                   framework's raw metadata buffers ("The Capture-Safe Kernel",
-//                   Decisions 1, 2 and 5).
-//   partial_kernel  one workgroup per work item: gathers the item's scattered
-//                   page_size=1 latent rows through kv_indices / out_cache_loc
-//                   into LDS ("The Integration Chasm", The Decision: Adapt the
-//                   Kernel, Not the System), computes S^T = K.Q^T and
+//   partial_kernel  every workgroup first works out the call's plan from the
+//                   serving framework's raw metadata buffers - per-request
+//                   lengths and checks, key-range length, the table of
+//                   (request, row block, key range) work items ("The
+//                   Capture-Safe Kernel", Decisions 1, 2 and 5) - and takes
+//                   its own item.  It gathers the item's scattered page_size=1
+//                   latent rows through kv_indices / out_cache_loc into LDS
+//                   ("The Integration Chasm", The Decision: Adapt the Kernel,
+//                   Not the System), builds the tree-visibility words of its
+//                   rows from custom_mask, computes S^T = K.Q^T and
 //                   O^T += V^T.P^T with bf16 MFMA and fp32 accumulation, keeps
-//                   an online softmax per query row, and writes the unnormalised
-//                   partial (O, running max, running sum) - the KV-split partial
-//                   of the pages' split-K design ("The Integration Chasm",
-//                   Context: What Came Before; "The Capture-Safe Kernel",
-//                   Decision 3).
+//                   an online softmax per query row, and writes the
+//                   unnormalised partial (O, running max, running sum) - the
+//                   KV-split partial of the pages' split-K design ("The
+//                   Integration Chasm", Context: What Came Before; "The
+//                   Capture-Safe Kernel", Decision 3).
 //   merge_kernel    combines the partial softmax statistics of each query row
 //                   across its key ranges ("The Capture-Safe Kernel", Decision 4)
 //                   into the normalised output and its log-sum-exp.
 //
-// The grids of all three depend on the plan only.
+// The grids of both depend on the plan only.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -51,6 +52,8 @@ constexpr int kRopeSlots = 3;
 __device__ __forceinline__ int vswz(int k) { return k & 15; }
 __device__ __forceinline__ int rswz(int k) { return (k >> 1) & 7; }
 constexpr int kTilesPerIdx = kIdxKeys / kKeysPerTile;    // 8
+constexpr int kRowUnits = kDqk * 2 / 16;   // 16-byte units per latent row
+constexpr int kMaxTree = MLA_VERIFY_MAX_TREE_NODES;
 constexpr float kRescaleSlack = 8.f;  // rescale O only when a row max grows by > 2^8
 
 // Key order inside a 32-key tile for the PV product.  Lane group g (lanes
@@ -59,198 +62,31 @@ constexpr float kRescaleSlack = 8.f;  // rescale O only when a row max grows by 
 // lanes hold in the S^T accumulators (rows 4g+i of each 16-key output tile),
 // so P moves from the softmax to the PV operand without any data exchange.
 
+// Row reductions over the four lane groups that hold one query row (lanes
+// n, n+16, n+32, n+48): the gfx950 swaps exchange 16-lane rows (xor 16) and
+// 32-lane halves (xor 32) in the VALU, with no LDS round trip.
+__device__ __forceinline__ float group_max(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ uint32_t group_or(uint32_t v) {
+  auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = a[0] | a[1];
+  auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return b[0] | b[1];
+}
+__device__ __forceinline__ float group_sum(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ int64_t load_index(const void* base, int64_t i, int is64) {
   return is64 ? reinterpret_cast<const int64_t*>(base)[i]
               : static_cast<int64_t>(reinterpret_cast<const int32_t*>(base)[i]);
-}
-
-// ---------------------------------------------------------------------------
-// slot staging (metadata launch, workgroups 1..): every request's keys in
-// combined order (prefix keys from kv_indices, then its tree nodes' own keys
-// from out_cache_loc), at kv_indptr[b] + qo_indptr[b] + j, as int32 pool
-// slots, -1 for a slot outside [0, num_slots).  The split-partial kernel then
-// reads one contiguous, checked int32 list per request.  A request whose
-// indptrs are out of range is skipped (workgroup 0 flags it and plans no
-// work); every read stays inside the ranges the indptrs were checked against.
-// ---------------------------------------------------------------------------
-// ---------------------------------------------------------------------------
-// metadata launch, workgroups 1..: per-key and per-token staging beside the
-// planning in workgroup 0.  Each group takes a contiguous share of the keys
-// and every groups-th token, and reads the index buffers within the ranges
-// the indptrs were checked against; a request whose indptrs or mask size are
-// out of range is skipped (workgroup 0 flags it and plans no work).
-//
-//   slots: every request's keys in combined order (prefix keys from
-//     kv_indices, then its tree nodes' own keys from out_cache_loc), at
-//     kv_indptr[b] + qo_indptr[b] + j, as int32 pool slots; -1 for a slot
-//     outside [0, num_slots), -2 for a prefix key whose full-row mask column
-//     hides it from some node (with the prefix check).  The split-partial
-//     kernel reads one contiguous, checked list per request.
-//   tree words: bit k of token t's word is its mask entry for tree node k of
-//     its request (T x T blocks, or full rows of P + T entries whose tree part
-//     starts at column P); one wave per token, lane k reads entry k and a
-//     ballot packs the row.
-//   fused KV save: draft token t's latent row kv_new[t] goes to pool slot
-//     out_cache_loc[t], 16 bytes per thread (72 per row), before the partial
-//     launch gathers it; slots outside the pool are not stored.
-// The loads of one pass are all issued before the first of them is used, so
-// a group waits for about two memory round trips.
-// ---------------------------------------------------------------------------
-constexpr int kRowUnits = kDqk * 2 / 16;   // 16-byte units per latent row
-__device__ void meta_staging(const KernelParams& p, int group, int groups) {
-  const int B = p.batch;
-  if (B <= 0) return;
-  // per request, in LDS: where its keys start, its prefix start and length,
-  // its first query token and key count (0 for a request whose indptrs are
-  // out of range)
-  __shared__ int s_start[kMaxBatch], s_k0[kMaxBatch], s_P[kMaxBatch], s_q0[kMaxBatch], s_N[kMaxBatch];
-  __shared__ int s_m0[kMaxBatch];   // full-row mask block of the request, -1 when not checked
-  __shared__ int s_tm0[kMaxBatch];  // tree columns of its node 0's mask row, -1 when unreadable
-  __shared__ int s_qB, s_kB;
-  const bool check_prefix = (p.flags & MLA_VERIFY_FLAG_CHECK_PREFIX_MASK) != 0;
-  const bool full_rows = (p.flags & MLA_VERIFY_FLAG_MASK_FULL_ROWS) != 0;
-  if (threadIdx.x == 0) {
-    s_qB = p.qo_indptr[B];
-    s_kB = p.kv_indptr[B];
-  }
-  for (int b = threadIdx.x; b < B; b += kMetaThreads) {
-    const int q0 = p.qo_indptr[b], q1 = p.qo_indptr[b + 1];
-    const int k0 = p.kv_indptr[b], k1 = p.kv_indptr[b + 1];
-    const int m0 = p.mask_indptr[b], m1 = p.mask_indptr[b + 1];
-    const bool ok = q0 >= 0 && q1 >= q0 && q1 <= p.max_q_tokens && k0 >= 0 && k1 >= k0 &&
-                    (int64_t)k1 <= p.max_kv_tokens;
-    s_start[b] = k0 + q0;
-    s_k0[b] = k0;
-    s_P[b] = k1 - k0;
-    s_q0[b] = q0;
-    s_N[b] = ok ? (k1 - k0) + (q1 - q0) : 0;
-    // mask rows are read only where the block has the size its layout gives
-    const long long T = q1 - q0;
-    const long long sq = T * T, full = T * ((long long)(k1 - k0) + T);
-    const bool m_ok = ok && m0 >= 0 && (long long)m1 - m0 == (full_rows ? full : sq);
-    s_m0[b] = (check_prefix && full_rows && m_ok) ? m0 : -1;
-    s_tm0[b] = (m_ok && T <= p.max_tree_nodes && T <= 64) ? m0 + (full_rows ? k1 - k0 : 0) : -1;
-  }
-  __syncthreads();
-  const int qB = s_qB, kB = s_kB;
-  if (qB < 0 || qB > p.max_q_tokens || kB < 0 || (int64_t)kB > p.max_kv_tokens) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int kW = kMetaThreads / 64;
-
-  // tree word of token t: where this lane's mask entry is, -1 when it has none
-  // (also for a whole row that is not read)
-  auto tree_entry = [&](int t) -> long long {
-    int lo = 0, hi = B - 1;   // last request whose tokens start at or before t
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_q0[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    const int m0 = s_tm0[lo];
-    const int T = s_N[lo] - s_P[lo];
-    const int i = t - s_q0[lo];
-    if (m0 < 0 || i < 0 || i >= T || lane >= T) return -1;
-    return (long long)m0 + (long long)i * (full_rows ? s_P[lo] + T : T) + lane;
-  };
-  auto tree_row_valid = [&](int t) {
-    // the row is written when its request's mask is readable (lane 0 always
-    // has an entry then, T >= 1)
-    return __builtin_amdgcn_readfirstlane((int)(tree_entry(t) >= 0 ? 1 : 0));
-  };
-  // this wave's first token: its entry is loaded now and packed after the
-  // slot loads below have been issued
-  const int t_first = group * kW + wave;
-  const long long e_first = t_first < qB ? tree_entry(t_first) : -1;
-  const int row_first = t_first < qB ? tree_row_valid(t_first) : 0;
-  const uint8_t m_first = e_first >= 0 ? p.custom_mask[e_first] : 0;
-
-  // fused KV save: this thread's first unit of the new rows (the rest below)
-  const int64_t units = p.kv_new ? (int64_t)qB * kRowUnits : 0;
-  const int64_t u_first = (int64_t)group * kMetaThreads + threadIdx.x;
-  u32x4 sv = u32x4{0u, 0u, 0u, 0u};
-  int64_t sslot = -1;
-  if (u_first < units) {
-    const int t = (int)(u_first / kRowUnits), c = (int)(u_first % kRowUnits);
-    sv = *reinterpret_cast<const u32x4*>(p.kv_new + (int64_t)t * p.kv_new_stride_tok + 8 * c);
-    sslot = load_index(p.out_cache_loc, t, p.ocl_idx64);
-  }
-
-  const int total = qB + kB;
-  const int per = (total + groups - 1) / groups;
-  const int g0 = group * per, g1 = min(total, g0 + per);
-  // kPer positions per thread at a time: every index load is issued before
-  // the first store.  A thread's positions only grow, so the request that
-  // holds one (the last request whose keys start at or before it) is found
-  // by walking forward from the one that held the previous position; the
-  // walk starts at the request of the group's first position.
-  constexpr int kPer = 8;
-  int lo = 0;
-  {
-    int hi = B - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_start[mid] <= g0) lo = mid; else hi = mid - 1;
-    }
-  }
-  int r_start = s_start[lo], r_next = lo + 1 < B ? s_start[lo + 1] : INT_MAX;
-  for (int base = g0; base < g1; base += kPer * kMetaThreads) {
-    int64_t raw[kPer];
-    bool have[kPer], hidden[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int g = base + k * kMetaThreads + (int)threadIdx.x;
-      have[k] = false;
-      hidden[k] = false;
-      raw[k] = 0;
-      if (g >= g1) continue;
-      while (g >= r_next) {
-        ++lo;
-        r_start = r_next;
-        r_next = lo + 1 < B ? s_start[lo + 1] : INT_MAX;
-      }
-      const int j = g - r_start;
-      if (j < 0 || j >= s_N[lo]) continue;
-      const int P = s_P[lo];
-      raw[k] = j < P ? load_index(p.kv_indices, (int64_t)s_k0[lo] + j, p.kv_idx64)
-                     : load_index(p.out_cache_loc, (int64_t)s_q0[lo] + (j - P), p.ocl_idx64);
-      have[k] = true;
-      if (j < P && s_m0[lo] >= 0) {
-        // column j of every node's full mask row must be nonzero
-        const int T = s_N[lo] - P;
-        const uint8_t* col = p.custom_mask + s_m0[lo] + j;
-        for (int i = 0; i < T; ++i) hidden[k] |= col[(size_t)i * (P + T)] == 0;
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      if (!have[k]) continue;
-      const int g = base + k * kMetaThreads + (int)threadIdx.x;
-      p.slots[g] = hidden[k] ? kSlotMaskedPrefix : (raw[k] >= 0 && raw[k] < p.num_slots) ? (int32_t)raw[k] : -1;
-      if (p.trace) p.trace[g] = raw[k];
-    }
-  }
-
-  {
-    const uint64_t w = __builtin_amdgcn_ballot_w64(m_first != 0);
-    if (row_first && lane == 0) p.anc[t_first] = w;
-  }
-  for (int t = t_first + groups * kW; t < qB; t += groups * kW) {
-    const long long e = tree_entry(t);
-    const int row = tree_row_valid(t);
-    const bool vis = e >= 0 && p.custom_mask[e] != 0;
-    const uint64_t w = __builtin_amdgcn_ballot_w64(vis);
-    if (row && lane == 0) p.anc[t] = w;
-  }
-
-  uint16_t* pool = const_cast<uint16_t*>(p.kv_pool);
-  for (int64_t u = u_first; u < units; u += (int64_t)groups * kMetaThreads) {
-    if (u != u_first) {
-      const int t = (int)(u / kRowUnits), c = (int)(u % kRowUnits);
-      sv = *reinterpret_cast<const u32x4*>(p.kv_new + (int64_t)t * p.kv_new_stride_tok + 8 * c);
-      sslot = load_index(p.out_cache_loc, t, p.ocl_idx64);
-    }
-    if (sslot < 0 || sslot >= p.num_slots) continue;
-    *reinterpret_cast<u32x4*>(pool + sslot * p.kv_row_stride + 8 * (int)(u % kRowUnits)) = sv;
-  }
 }
 
 // ceil(a / b) for a >= 0, b >= 1: the 32-bit division when both fit, which
@@ -264,51 +100,219 @@ __device__ __forceinline__ long long div_up(long long a, long long b) {
 }
 
 // ---------------------------------------------------------------------------
-// metadata build: workgroup 0 (the slot staging runs beside it)
+// the plan of a call, computed on the device from the serving framework's
+// raw metadata buffers ("The Capture-Safe Kernel", Decisions 1, 2 and 5):
+// every workgroup of the split-partial launch works out the same plan, so no
+// launch has to build it first and the grid stays fixed by the host plan
+// (Decision 3).
+//
+// Per request b: T_b = qo_indptr[b+1] - qo_indptr[b], P_b = kv_indptr[b+1] -
+// kv_indptr[b] (Decision 2), the checks behind the metadata error bits, and
+// its query rows (node, head), heads fastest, cut into 64-row blocks.  Each
+// request's combined key range [0, P_b + T_b) is cut into ranges of one
+// length shared by all requests, rounded to 32 keys and at least 128.  Five
+// candidate lengths cut the total work W = sum_b rowblocks_b (P_b + T_b) into
+// about target_items pieces, or m target_items - sum_b rowblocks_b pieces for
+// m = 1..4 (each row block adds at most one partly filled range); the one
+// with the least modelled time - rounds of target_items workgroups x (tiles
+// per range + the per-item cost, about kItemTiles tiles) - among those whose
+// items fit the plan is taken.  Work items are numbered request by request,
+// then key range, then row block.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
-  if (blockIdx.x > 0) {
-    meta_staging(p, blockIdx.x - 1, gridDim.x - 1);
-    return;
-  }
-  __shared__ int32_t s_req[kMaxBatch][8];
-  __shared__ uint32_t s_err;
-  __shared__ long long s_work;
-  __shared__ int s_rowblocks;
-  constexpr int kCands = 5;
-  __shared__ int s_scan[kMetaThreads / 64];
-  __shared__ int s_cand[kCands];
-  __shared__ int s_cand_items[kCands];
-  __shared__ long long s_cand_cost[kCands];
-  __shared__ int32_t s_chunk;
-  __shared__ int32_t s_items;
-  __shared__ int32_t s_total_q;
-  __shared__ int32_t s_max_chunks;
-  const int tid = threadIdx.x;
+constexpr int kCands = 5;
+constexpr long long kItemTiles = 6;
+constexpr int kPlanWaves = kPartialThreads / 64;
+struct PlanShared {
+  long long w_work[kPlanWaves];        // per-wave partial sums
+  int w_rowblocks[kPlanWaves];
+  uint32_t w_err[kPlanWaves];
+  int w_items[kPlanWaves][kCands];
+  int w_scan[kPlanWaves];
+  int w_most[kPlanWaves];
+  int total_q;
+  // the plan
+  uint32_t err;
+  int chunk;
+  int items;
+  int max_chunks;
+};
+
+template <typename V>
+__device__ __forceinline__ V wave_sum(V v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v |= (uint32_t)__shfl_xor((int)v, d);
+  return v;
+}
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = max(v, __shfl_xor(v, d));
+  return v;
+}
+
+// Reductions over the 64 lanes of a wave, result in every lane: rotations
+// inside each 16-lane row (DPP, fused into the add), then the gfx950 row
+// swaps across rows.  A few VALU instructions, no LDS round trip.
+__device__ __forceinline__ int dpp_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x128, 0xf, 0xf, false);   // row_ror:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x124, 0xf, 0xf, false);   // row_ror:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x122, 0xf, 0xf, false);   // row_ror:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x121, 0xf, 0xf, false);   // row_ror:1
+  auto a = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  v = (int)(a[0] + a[1]);
+  auto c = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  return (int)(c[0] + c[1]);
+}
+__device__ __forceinline__ int dpp_max(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x128, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x124, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x122, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x121, 0xf, 0xf, false));
+  auto a = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  v = max((int)a[0], (int)a[1]);
+  auto c = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  return max((int)c[0], (int)c[1]);
+}
+__device__ __forceinline__ uint32_t dpp_or(uint32_t v) {
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false);
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false);
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xf, 0xf, false);
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xf, 0xf, false);
+  auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = a[0] | a[1];
+  auto c = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return c[0] | c[1];
+}
+// a request's item count under key-range length c, capped so that sums of
+// kMaxBatch of them stay in 32 bits (a count that large never fits a plan)
+constexpr int kItemsCap = 1 << 20;
+
+// The plan for at most 64 requests, by one wave (lane b = request b): one
+// global round trip for the indptrs, then DPP reductions; no barrier.  The
+// total work is summed in float, which is exact enough to pick a range
+// length and, being the same sum in every workgroup, gives every workgroup
+// the same plan.
+__device__ void plan_call_wave(const KernelParams& p, int32_t (*req)[8], PlanShared& sp) {
+  const int lane = threadIdx.x & 63;
   const int B = p.batch;
   const int H = p.num_heads;
-  if (tid == 0) {
-    s_err = 0;
-    s_work = 0;
-    s_rowblocks = 0;
-    s_items = 0;
-    s_max_chunks = 0;
-    for (int m = 0; m < kCands; ++m) s_cand_items[m] = 0;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    // query tokens of the call, clamped to the plan's bound
-    int tq = B > 0 ? p.qo_indptr[B] : 0;
-    s_total_q = tq < 0 ? 0 : (tq > p.max_q_tokens ? p.max_q_tokens : tq);
-  }
-
-  // per-request lengths and checks (prefix length = kv_indptr[b+1] - kv_indptr[b])
   const bool full_rows = (p.flags & MLA_VERIFY_FLAG_MASK_FULL_ROWS) != 0;
-  if (tid < (int)(sizeof(mla_verify_compare_stats_t) / 4)) reinterpret_cast<uint32_t*>(p.stats)[tid] = 0;
+  const bool have = lane < B;
+  int q0 = 0, q1 = 0, k0 = 0, k1 = 0, m0 = 0, m1 = 0;
+  if (have) {
+    q0 = p.qo_indptr[lane];
+    q1 = p.qo_indptr[lane + 1];
+    k0 = p.kv_indptr[lane];
+    k1 = p.kv_indptr[lane + 1];
+    m0 = p.mask_indptr[lane];
+    m1 = p.mask_indptr[lane + 1];
+  }
+  const int T = q1 - q0, P = k1 - k0;
+  uint32_t err = 0;
+  if (have) {
+    if (q0 < 0 || T < 0 || q1 > p.max_q_tokens || (lane == 0 && q0 != 0)) err |= MLA_VERIFY_DEVERR_QO_INDPTR;
+    if (k0 < 0 || P < 0 || (long long)k1 > p.max_kv_tokens) err |= MLA_VERIFY_DEVERR_KV_INDPTR;
+    if (T > p.max_tree_nodes) err |= MLA_VERIFY_DEVERR_TREE_SIZE;
+    const long long mask_size = full_rows ? (long long)T * ((long long)T + P) : (long long)T * T;
+    if (m0 < 0 || (long long)(m1 - m0) != mask_size) err |= MLA_VERIFY_DEVERR_MASK_INDPTR;
+  }
+  const int Tc = T < 0 ? 0 : T, Pc = P < 0 ? 0 : P;
+  const int N = Pc + Tc;
+  const int rb = (int)(((long long)Tc * H + kRowsPerItem - 1) / kRowsPerItem);
+  if (have) {
+    req[lane][RQ_P] = Pc;
+    req[lane][RQ_T] = Tc;
+    req[lane][RQ_Q0] = q0;
+    req[lane][RQ_KV0] = k0;
+    req[lane][RQ_RB] = rb;
+    req[lane][RQ_MASK0] = m0;
+  }
+  err = dpp_or(err);
+  const int rowblocks = dpp_sum(rb);
+  float workf = (float)rb * (float)N;
+  workf += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, workf), 0x128, 0xf, 0xf, false));
+  workf += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, workf), 0x124, 0xf, 0xf, false));
+  workf += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, workf), 0x122, 0xf, 0xf, false));
+  workf += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, workf), 0x121, 0xf, 0xf, false));
+  workf = group_sum(workf);
+  auto items_of = [&](int c) {   // this lane's request under range length c
+    return rb > 0 ? (int)min((long long)rb * ((N + c - 1) / c), (long long)kItemsCap) : 0;
+  };
+  int chunk_sel = 0;
+  float best = -1.f;
+  const float inv_target = 1.f / (float)p.target_items;
+#pragma unroll
+  for (int m = 0; m < kCands; ++m) {
+    float slots = m == 0 ? (float)p.target_items : (float)m * p.target_items - rowblocks;
+    if (slots < 1.f) slots = 1.f;
+    const float per = ceilf(workf / slots);
+    int c = per >= (float)(1 << 30) ? (1 << 30) : ((int)per + kKeysPerTile - 1) / kKeysPerTile * kKeysPerTile;
+    if (c < kMinChunkKeys) c = kMinChunkKeys;
+    const int items = dpp_sum(items_of(c));
+    // modelled time: rounds of target_items workgroups x (tiles per range +
+    // the per-item cost); float, so that it takes no integer division
+    const float rounds = fmaxf(1.f, ceilf((float)items * inv_target));
+    const float cost = items > p.item_capacity ? -1.f : rounds * (float)(c / kKeysPerTile + kItemTiles);
+    if (m == 0) chunk_sel = c;   // none fits: cand[0], flagged below
+    if (cost >= 0.f && (best < 0.f || cost < best)) {
+      best = cost;
+      chunk_sel = c;
+    }
+  }
+  // each request's first item: an inclusive scan of the item counts over the
+  // lanes (DPP: shifts inside each 16-lane row, then the last lane of a row
+  // broadcast into the rows after it), less the lane's own count
+  const int mine = items_of(chunk_sel);
+  int incl = mine;
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xf, 0xf, false);   // row_shr:1
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xf, 0xf, false);   // row_shr:2
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xf, 0xf, false);   // row_shr:4
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xf, 0xf, false);   // row_shr:8
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x142, 0xa, 0xf, false);   // row_bcast:15 into rows 1, 3
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x143, 0xc, 0xf, false);   // row_bcast:31 into rows 2, 3
+  const int all_items = __builtin_amdgcn_readlane(incl, 63);
+  const int chunks = rb > 0 ? (N + chunk_sel - 1) / chunk_sel : 0;
+  if (have) {
+    req[lane][RQ_CHUNKS] = chunks;
+    req[lane][RQ_ITEM0] = incl - mine;
+  }
+  const int most = dpp_max(chunks);
+  const int tq = B > 0 ? __builtin_amdgcn_readlane(q1, B - 1) : 0;
+  if (lane == 0) {
+    if (all_items > p.item_capacity) err |= MLA_VERIFY_DEVERR_CAPACITY;
+    sp.err = err;
+    sp.chunk = chunk_sel;
+    sp.items = (err & kMetaErrMask) ? 0 : all_items;
+    sp.max_chunks = most;
+    sp.total_q = tq < 0 ? 0 : (tq > p.max_q_tokens ? p.max_q_tokens : tq);
+  }
+}
+
+// req: kMaxBatch x 8 int32 of LDS (RQ_* columns).  Up to 64 requests: one
+// wave (above).  More: every thread takes requests, one global round trip,
+// wave reductions and four barriers.  Ends with a barrier, after which sp's
+// plan fields and req hold the plan.
+__device__ void plan_call(const KernelParams& p, int32_t (*req)[8], PlanShared& sp) {
+  if (p.batch <= 64) {
+    if (threadIdx.x < 64) plan_call_wave(p, req, sp);
+    __syncthreads();
+    return;
+  }
+  constexpr int kThreads = kPartialThreads;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int B = p.batch;
+  const int H = p.num_heads;
+  const bool full_rows = (p.flags & MLA_VERIFY_FLAG_MASK_FULL_ROWS) != 0;
   uint32_t err = 0;
   long long work = 0;
   int rowblocks = 0;
-  for (int b = tid; b < B; b += kMetaThreads) {
+  if (tid == 0 && B <= 0) sp.total_q = 0;
+  for (int b = tid; b < B; b += kThreads) {
     const int q0 = p.qo_indptr[b], q1 = p.qo_indptr[b + 1];
     const int k0 = p.kv_indptr[b], k1 = p.kv_indptr[b + 1];
     const int m0 = p.mask_indptr[b], m1 = p.mask_indptr[b + 1];
@@ -319,72 +323,82 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
     const long long mask_size = full_rows ? (long long)T * ((long long)T + P) : (long long)T * T;
     if (m0 < 0 || (long long)(m1 - m0) != mask_size) err |= MLA_VERIFY_DEVERR_MASK_INDPTR;
     const int Tc = T < 0 ? 0 : T, Pc = P < 0 ? 0 : P;
-    const int rows = Tc * H;
-    const int rb = (rows + kRowsPerItem - 1) / kRowsPerItem;
-    s_req[b][RQ_P] = Pc;
-    s_req[b][RQ_T] = Tc;
-    s_req[b][RQ_Q0] = q0;
-    s_req[b][RQ_KV0] = k0;
-    s_req[b][RQ_RB] = rb;
-    s_req[b][RQ_MASK0] = m0;
+    const int rb = (Tc * H + kRowsPerItem - 1) / kRowsPerItem;
+    req[b][RQ_P] = Pc;
+    req[b][RQ_T] = Tc;
+    req[b][RQ_Q0] = q0;
+    req[b][RQ_KV0] = k0;
+    req[b][RQ_RB] = rb;
+    req[b][RQ_MASK0] = m0;
     work += (long long)rb * (Pc + Tc);
     rowblocks += rb;
+    // query tokens of the call (qo_indptr[B]), clamped to the plan's bound
+    if (b == B - 1) sp.total_q = q1 < 0 ? 0 : (q1 > p.max_q_tokens ? p.max_q_tokens : q1);
   }
-  if (err) atomicOr(&s_err, err);
-  if (work) atomicAdd(reinterpret_cast<unsigned long long*>(&s_work), (unsigned long long)work);
-  if (rowblocks) atomicAdd(&s_rowblocks, rowblocks);
+  work = wave_sum(work);
+  rowblocks = wave_sum(rowblocks);
+  err = wave_or(err);
+  if (lane == 0) {
+    sp.w_work[wv] = work;
+    sp.w_rowblocks[wv] = rowblocks;
+    sp.w_err[wv] = err;
+  }
   __syncthreads();
+  work = 0;
+  rowblocks = 0;
+  err = 0;
+#pragma unroll
+  for (int w = 0; w < kPlanWaves; ++w) {
+    work += sp.w_work[w];
+    rowblocks += sp.w_rowblocks[w];
+    err |= sp.w_err[w];
+  }
 
-  // key-range length shared by all requests.  Candidates cut the total (row
-  // block x key) work into about m x target_items pieces (less the row-block
-  // count, since every row block adds at most one partly filled range),
-  // rounded up to whole tiles; the one chosen has the least modelled time:
-  // rounds of target_items workgroups x (tiles per range + the per-item
-  // cost, about kItemTiles tiles), among those whose items fit the plan.
-  // Thread m works out candidate m, so the 64-bit divisions run side by side.
+  // key-range length shared by all requests; every thread works out the
+  // candidates (no barrier): they cut the total work into about
+  // m x target_items pieces, less the row-block count for m >= 1 (each row
+  // block adds at most one partly filled range), rounded up to whole tiles
   auto items_of = [&](int b, int c) {
-    const int N = s_req[b][RQ_P] + s_req[b][RQ_T];
-    const int rb = s_req[b][RQ_RB];
+    const int N = req[b][RQ_P] + req[b][RQ_T];
+    const int rb = req[b][RQ_RB];
     return rb > 0 ? rb * ((N + c - 1) / c) : 0;
   };
-  constexpr long long kItemTiles = 6;
-  if (tid < kCands) {
-    long long slots = tid == 0 ? (long long)p.target_items : (long long)tid * p.target_items - s_rowblocks;
+  int cand[kCands];
+#pragma unroll
+  for (int m = 0; m < kCands; ++m) {
+    long long slots = m == 0 ? (long long)p.target_items : (long long)m * p.target_items - rowblocks;
     if (slots < 1) slots = 1;
-    const long long per_item = div_up(s_work, slots);
+    const long long per_item = div_up(work, slots);
     long long c = ((per_item + kKeysPerTile - 1) / kKeysPerTile) * kKeysPerTile;
     if (c < kMinChunkKeys) c = kMinChunkKeys;
     if (c > (1LL << 30)) c = 1LL << 30;
-    s_cand[tid] = (int)c;
+    cand[m] = (int)c;
   }
-  __syncthreads();
-  int cand[kCands];
-#pragma unroll
-  for (int m = 0; m < kCands; ++m) cand[m] = s_cand[m];
   {
     int mine[kCands] = {0, 0, 0, 0, 0};
-    for (int b = tid; b < B; b += kMetaThreads)
+    for (int b = tid; b < B; b += kThreads)
 #pragma unroll
       for (int m = 0; m < kCands; ++m) mine[m] += items_of(b, cand[m]);
 #pragma unroll
-    for (int m = 0; m < kCands; ++m)
-      if (mine[m]) atomicAdd(&s_cand_items[m], mine[m]);   // zeroed at the start
+    for (int m = 0; m < kCands; ++m) {
+      const int t = wave_sum(mine[m]);
+      if (lane == 0) sp.w_items[wv][m] = t;
+    }
   }
   __syncthreads();
-  if (tid < kCands) {
-    // modelled cost of candidate m, -1 when its items do not fit
-    const long long items = s_cand_items[tid];
-    const long long rounds = div_up(items, (long long)p.target_items);
-    s_cand_cost[tid] = items > p.item_capacity ? -1 : (rounds < 1 ? 1 : rounds) * (cand[tid] / kKeysPerTile + kItemTiles);
-  }
-  __syncthreads();
-  // the first candidate of least cost; none fits: cand[0], flagged below
+  // the candidate with the least modelled time: rounds of target_items
+  // workgroups x (tiles per range + the per-item cost, about kItemTiles
+  // tiles), among those whose items fit the plan; none fits: cand[0], flagged
   int chunk_sel = cand[0];
   {
     long long best = -1;
 #pragma unroll
     for (int m = 0; m < kCands; ++m) {
-      const long long cost = s_cand_cost[m];
+      long long items = 0;
+#pragma unroll
+      for (int w = 0; w < kPlanWaves; ++w) items += sp.w_items[w][m];
+      const long long rounds = div_up(items, (long long)p.target_items);
+      const long long cost = items > p.item_capacity ? -1 : (rounds < 1 ? 1 : rounds) * (cand[m] / kKeysPerTile + kItemTiles);
       if (cost >= 0 && (best < 0 || cost < best)) {
         best = cost;
         chunk_sel = cand[m];
@@ -394,112 +408,96 @@ __global__ __launch_bounds__(kMetaThreads) void meta_kernel(KernelParams p) {
   // each request's first item: an exclusive scan of the item counts over
   // contiguous runs of requests per thread, inside each wave by shuffles and
   // across the waves through LDS
-  const int run = (B + kMetaThreads - 1) / kMetaThreads;
+  const int run = (B + kThreads - 1) / kThreads;
   const int b_lo = min(B, tid * run), b_hi = min(B, b_lo + run);
   int local = 0;
   for (int b = b_lo; b < b_hi; ++b) local += items_of(b, chunk_sel);
-  const int lane = tid & 63, wv = tid >> 6;
   int incl = local;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const int y = __shfl_up(incl, d);
     if (lane >= d) incl += y;
   }
-  if (lane == 63) s_scan[wv] = incl;
+  if (lane == 63) sp.w_scan[wv] = incl;
   __syncthreads();
   int before = 0, all_items = 0;
 #pragma unroll
-  for (int w = 0; w < kMetaThreads / 64; ++w) {
-    const int x = s_scan[w];
+  for (int w = 0; w < kPlanWaves; ++w) {
+    const int x = sp.w_scan[w];
     before += w < wv ? x : 0;
     all_items += x;
   }
+  int most = 0;
   {
     int at = before + incl - local;
-    int most = 0;
     for (int b = b_lo; b < b_hi; ++b) {
-      const int N = s_req[b][RQ_P] + s_req[b][RQ_T];
-      const int rb = s_req[b][RQ_RB];
+      const int N = req[b][RQ_P] + req[b][RQ_T];
+      const int rb = req[b][RQ_RB];
       const int chunks = rb > 0 ? (N + chunk_sel - 1) / chunk_sel : 0;
-      s_req[b][RQ_CHUNKS] = chunks;
-      s_req[b][RQ_ITEM0] = at;
+      req[b][RQ_CHUNKS] = chunks;
+      req[b][RQ_ITEM0] = at;
       at += items_of(b, chunk_sel);
       most = max(most, chunks);
     }
-    if (most) atomicMax(&s_max_chunks, most);
   }
+  most = wave_max(most);
+  if (lane == 0) sp.w_most[wv] = most;
   __syncthreads();
   if (tid == 0) {
-    int items = all_items;
-    s_chunk = chunk_sel;
-    if (items > p.item_capacity) s_err |= MLA_VERIFY_DEVERR_CAPACITY;
-    if (s_err & kMetaErrMask) items = 0;
-    s_items = items;
-  }
-  __syncthreads();
-  const int chunk = s_chunk;
-  const int n_items = s_items;
-
-  for (int b = tid; b < B; b += kMetaThreads) {
+    int m = 0;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) p.req[b * 8 + c] = s_req[b][c];
+    for (int w = 0; w < kPlanWaves; ++w) m = max(m, sp.w_most[w]);
+    if (all_items > p.item_capacity) err |= MLA_VERIFY_DEVERR_CAPACITY;
+    sp.err = err;
+    sp.chunk = chunk_sel;
+    sp.items = (err & kMetaErrMask) ? 0 : all_items;
+    sp.max_chunks = m;
   }
-  // work items: request, row block, key range [key0, key1) in combined order,
-  // and for every split-partial workgroup its launch entry.  Workgroup g runs
-  // on XCD g % 8 and takes item (g % 8) * per_xcd + g / 8, so the items of a
-  // key range (consecutive, one per row block) share that XCD's L2; the entry
-  // holds all the item's fields the workgroup needs, so it starts with one
-  // load.
-  const int per_xcd = (n_items + 7) >> 3;
-  for (int g = tid; g < p.partial_grid; g += kMetaThreads) {
-    const int it = (g & 7) * per_xcd + (g >> 3);
-    int32_t* ln = p.launch + (size_t)g * 8;
-    if ((g >> 3) >= per_xcd || it >= n_items) {
-      *reinterpret_cast<i32x4*>(ln) = i32x4{-1, 0, 0, 0};
-      continue;
-    }
-    int lo = 0, hi = B - 1;
-    while (lo < hi) {  // last request whose first item is <= it
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_req[mid][RQ_ITEM0] <= it) lo = mid; else hi = mid - 1;
-    }
-    const int b = lo;
-    const int rbs = s_req[b][RQ_RB];
-    const int local = it - s_req[b][RQ_ITEM0];
-    const int c = local / rbs, rb = local % rbs;
-    const int N = s_req[b][RQ_P] + s_req[b][RQ_T];
-    const int key0 = c * chunk;
-    const int key1 = min(N, key0 + chunk);
-    const int rows = s_req[b][RQ_T] * H;
-    const int row0 = rb * kRowsPerItem;
-    const int nrows = min(kRowsPerItem, rows - row0);
-    int32_t* e = p.items + (size_t)it * 8;
-    *reinterpret_cast<i32x4*>(e) = i32x4{b, rb, c, key0};
-    *reinterpret_cast<i32x4*>(e + 4) = i32x4{key1, row0, nrows, 0};
-    *reinterpret_cast<i32x4*>(ln) = i32x4{it, key0, key1, row0};
-    *reinterpret_cast<i32x4*>(ln + 4) =
-        i32x4{nrows, s_req[b][RQ_P], s_req[b][RQ_Q0], s_req[b][RQ_KV0] + s_req[b][RQ_Q0]};
+  __syncthreads();
+}
+
+// Last request whose column `col` (a non-decreasing start: RQ_Q0 or
+// RQ_ITEM0) is <= x; requests with nothing at x come before the one that
+// owns it, so the last one is the owner.
+__device__ __forceinline__ int find_request(const int32_t (*req)[8], int B, int col, int x) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (req[mid][col] <= x) lo = mid; else hi = mid - 1;
   }
-  // per query token, for the merge: its request's first token, first item,
-  // row blocks and key ranges (one 16-byte entry, so the merge reads no
-  // request table)
-  for (int t = tid; t < s_total_q; t += kMetaThreads) {
-    int lo = 0, hi = B - 1;   // last request whose tokens start at or before t
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_req[mid][RQ_Q0] <= t) lo = mid; else hi = mid - 1;
+  return lo;
+}
+
+// What workgroup 0 of the split-partial launch publishes for the merge and for
+// inspection: the header, the request table, and zeroed comparison
+// statistics; every workgroup writes the merge's entries of the tokens
+// t = blockIdx.x + k * gridDim.x (its request's first token, first item, row
+// blocks and key ranges, one 16-byte entry, so the merge searches no table).
+__device__ void publish_plan(const KernelParams& p, const int32_t (*req)[8], const PlanShared& sp) {
+  const int tid = threadIdx.x;
+  const int B = p.batch;
+  if (blockIdx.x == 0) {
+    for (int b = tid; b < B; b += kPartialThreads) {
+      *reinterpret_cast<i32x4*>(p.req + b * 8) = *reinterpret_cast<const i32x4*>(&req[b][0]);
+      *reinterpret_cast<i32x4*>(p.req + b * 8 + 4) = *reinterpret_cast<const i32x4*>(&req[b][4]);
     }
+    if (tid < (int)(sizeof(mla_verify_compare_stats_t) / 4)) reinterpret_cast<uint32_t*>(p.stats)[tid] = 0;
+    if (tid == 0) {
+      WsHeader* h = p.hdr;
+      h->err = sp.err;
+      h->err_meta = sp.err;
+      h->n_items = sp.items;
+      h->total_q = sp.total_q;
+      h->chunk_keys = sp.chunk;
+      h->batch = B;
+      h->max_chunks = sp.max_chunks;
+    }
+  }
+  const int step = (int)gridDim.x * kPartialThreads;
+  for (int t = (int)blockIdx.x + tid * (int)gridDim.x; t < sp.total_q; t += step) {
+    const int b = find_request(req, B, RQ_Q0, t);
     *reinterpret_cast<i32x4*>(p.tok + 4 * (size_t)t) =
-        i32x4{s_req[lo][RQ_Q0], s_req[lo][RQ_ITEM0], s_req[lo][RQ_RB], s_req[lo][RQ_CHUNKS]};
-  }
-  if (tid == 0) {
-    const int tq = s_total_q;
-    p.hdr->err = s_err;
-    p.hdr->n_items = n_items;
-    p.hdr->total_q = tq;
-    p.hdr->chunk_keys = chunk;
-    p.hdr->batch = B;
-    p.hdr->max_chunks = s_max_chunks;
+        i32x4{req[b][RQ_Q0], req[b][RQ_ITEM0], req[b][RQ_RB], req[b][RQ_CHUNKS]};
   }
 }
 
@@ -539,9 +537,14 @@ __device__ __forceinline__ void wait_vm_barrier(int n) {
 __device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
   return (uint32_t)(uintptr_t)MLAV_LDS(const void, ptr);
 }
-// row: wave-uniform global address; lane_off: this lane's byte offset from it
+// row: wave-uniform global address (moved to scalar registers here, so the
+// scalar operand holds whatever path computed it); lane_off: this lane's byte
+// offset from it
 __device__ __forceinline__ void dma16_row(const void* row, uint32_t lane_off, uint32_t lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(lane_off), "s"(row), "{m0}"(lds) : "memory");
+  const uint64_t a = (uint64_t)(uintptr_t)row;
+  const uint64_t sa = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(lane_off), "s"(sa), "{m0}"(lds) : "memory");
 }
 // addr: this lane's global address
 __device__ __forceinline__ void dma16(const void* addr, uint32_t lds) {
@@ -549,22 +552,6 @@ __device__ __forceinline__ void dma16(const void* addr, uint32_t lds) {
 }
 __device__ __forceinline__ void dma4(const void* addr, uint32_t lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" :: "v"(addr), "{m0}"(lds) : "memory");
-}
-
-// Row reductions over the four lane groups that hold one query row (lanes
-// n, n+16, n+32, n+48): the gfx950 swaps exchange 16-lane rows (xor 16) and
-// 32-lane halves (xor 32) in the VALU, with no LDS round trip.
-__device__ __forceinline__ float group_max(float v) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float group_sum(float v) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 constexpr int kKRing = 8;                  // K operand reads in flight ahead of the S MFMAs
@@ -580,51 +567,161 @@ static_assert(kTilesPerIdx >= 5, "an index block is loaded five tiles ahead of i
 // tiles that can hold no row.
 template <int kRowTilesMax>
 __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char s_v[kStages * kVSlotBytes];
+  __shared__ __attribute__((aligned(128))) unsigned char s_v[kStages * kVSlotBytes];
   __shared__ __attribute__((aligned(16))) unsigned char s_r[kRopeSlots * kRopeSlotBytes];
   __shared__ bf16x8 s_p[2][kWaves][2][64];      // P(i) in buffer i & 1: row tile, hi/lo, lane
-  __shared__ __attribute__((aligned(16))) int32_t s_idx[2][kIdxKeys];   // slot blocks (double buffered)
-  __shared__ f32x4 s_alpha[2][16];              // [i & 1][n][rt]: rescale factor of row 16rt + n
-  __shared__ uint32_t s_rescale[2];             // byte rt != 0 when row tile rt rescaled
+  __shared__ __attribute__((aligned(16))) uint32_t s_idx[2][kIdxKeys];   // raw slot words of key blocks (double buffered)
+  __shared__ f32x4 s_alpha[3][16];              // [i % 3][n][rt]: rescale factor of row 16rt + n
+  __shared__ uint32_t s_rescale[3];             // [i % 3]: byte rt != 0 when row tile rt rescaled
+  __shared__ uint32_t s_tree_hi[kMaxTree];       // high words of the item's 64-bit tree slots
+  __shared__ PlanShared sp;
+  static_assert(sizeof(s_v) >= sizeof(int32_t) * kMaxBatch * 8, "the plan tables fit in the V ring");
 
-  // Work items of one key range sit on one XCD: workgroup b is dispatched to
-  // XCD b % 8, so XCD x gets the contiguous items [x*per, (x+1)*per) and the
-  // row blocks that share a key range share that XCD's L2.
-  // this workgroup's launch entry (written by the metadata launch, which
-  // places the items of a key range on one XCD): item, key range, rows, and
-  // its request's prefix length, first token and slot list
+  const int tid = threadIdx.x;
   const int bid = blockIdx.x;
-  const i32x4 la = *reinterpret_cast<const i32x4*>(p.launch + (size_t)bid * 8);
-  const i32x4 lb = *reinterpret_cast<const i32x4*>(p.launch + (size_t)bid * 8 + 4);
-  const int item = la[0];
-  if (item < 0) return;
-  const int key0 = la[1], key1 = la[2], row0 = la[3];
-  const int nrows = lb[0], P = lb[1], q0 = lb[2], slot0 = lb[3];
   const int H = p.num_heads;
+
+  // ---- the call's plan, from the raw metadata; its per-request table lives
+  // in the V ring until the first tile loads
+  int32_t (*req)[8] = reinterpret_cast<int32_t (*)[8]>(s_v);
+  plan_call(p, req, sp);
+  publish_plan(p, req, sp);
+  // This workgroup's items.  About one workgroup per compute unit, each
+  // running its items one after another.  Workgroup g is dispatched to XCD
+  // g % 8; XCD x owns the contiguous items [x per, (x + 1) per) (per =
+  // ceil(items / 8)), taken by its workgroups in turn, so the row blocks that
+  // share a key range (consecutive items) run side by side on one XCD and
+  // share its L2.  The plan gives no workgroup more than kMaxItemsPerWg.
+  __shared__ int32_t s_mine[kMaxItemsPerWg][12];
+  __shared__ int s_nmine;
+  {
+    const int n_items = sp.items;
+    const int g8 = (int)gridDim.x >> 3, x = bid & 7;
+    const int per_xcd = (n_items + 7) >> 3;
+    const int first = x * per_xcd + (bid >> 3), last = min(n_items, (x + 1) * per_xcd);
+    const int count = first < last ? (last - first + g8 - 1) / g8 : 0;
+    if (tid < min(count, kMaxItemsPerWg)) {
+      const int item = first + tid * g8;
+      const int b = find_request(req, p.batch, RQ_ITEM0, item);
+      const int rbs = req[b][RQ_RB];
+      const int local_item = item - req[b][RQ_ITEM0];
+      const int chunk_no = local_item / rbs;
+      const int P = req[b][RQ_P], T = req[b][RQ_T];
+      const int key0 = chunk_no * sp.chunk;
+      int32_t* e = s_mine[tid];
+      e[0] = item;
+      e[1] = b;
+      e[2] = local_item % rbs;
+      e[3] = chunk_no;
+      e[4] = P;
+      e[5] = T;
+      e[6] = req[b][RQ_Q0];
+      e[7] = req[b][RQ_KV0];
+      e[8] = req[b][RQ_MASK0];
+      e[9] = key0;
+      e[10] = min(P + T, key0 + sp.chunk);
+    }
+    if (tid == 0) s_nmine = count;
+  }
+  __syncthreads();   // the plan tables are read
+  // (values read from LDS are the same in every lane: readfirstlane keeps
+  // them, and everything derived from them, in scalar registers)
+  auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+  uint32_t errbits = 0;   // this workgroup's device error bits (thread 0)
+  const int n_mine = uni(s_nmine);
+  if (n_mine > kMaxItemsPerWg) errbits |= MLA_VERIFY_DEVERR_CAPACITY;
+  // The item body, compiled once per role, so that each role's item loop
+  // keeps only its own loop-invariant values.
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  auto run_item = [&](int mi, auto role) {
+  constexpr bool kScore = decltype(role)::value;
+  const int item = uni(s_mine[mi][0]);
+  const int b = uni(s_mine[mi][1]), rb = uni(s_mine[mi][2]), chunk_no = uni(s_mine[mi][3]);
+  const int P = uni(s_mine[mi][4]), T = uni(s_mine[mi][5]);
+  const int q0 = uni(s_mine[mi][6]), kv0 = uni(s_mine[mi][7]), m0 = uni(s_mine[mi][8]);
+  const int key0 = uni(s_mine[mi][9]), key1 = uni(s_mine[mi][10]);
+  const int row0 = rb * kRowsPerItem;
+  const int nrows = min(kRowsPerItem, T * H - row0);
+  if (tid == 0) {
+    int32_t* e = p.items + (size_t)item * 8;
+    *reinterpret_cast<i32x4*>(e) = i32x4{b, rb, chunk_no, key0};
+    *reinterpret_cast<i32x4*>(e + 4) = i32x4{key1, row0, nrows, 0};
+  }
   const int ntiles = (key1 - key0 + kKeysPerTile - 1) / kKeysPerTile;
   const int nrt = (nrows + 15) >> 4;            // row tiles with at least one row
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool score_wave = wave < kWaves;
-  const int r = score_wave ? wave : wave - kWaves;   // row tile (score) or dim eighth (PV)
+  const int r = kScore ? wave : wave - kWaves;   // row tile (score) or dim eighth (PV)
   const int n = lane & 15, g = lane >> 4;
-
   const int r_local = 16 * r + n;
-  // this request's checked slots, prefix keys then tree nodes
-  const int32_t* kslots = p.slots + slot0;
 
-  // ---- slots: blocks of kIdxKeys keys staged in LDS (double buffered) ----
-  // The score waves copy the int32 slots of block b straight into LDS, lane
-  // = key, with the tile loads.  Keys past the range end re-read the range's
-  // last slot.  A slot of -1 (outside the pool) or -2 (a prefix key that a
-  // checked full-row mask hides) reads slot 0 instead and poisons the item:
-  // its rows become NaN.
-  bool out_of_pool = false, hidden = false;
+  // ---- where the keys' slots come from: prefix key j < P from
+  // kv_indices[kv0 + j], tree key j >= P from out_cache_loc[q0 + j - P],
+  // each int32 or int64 as the plan says.  The tile loop reads the low 32
+  // bits of each index (little-endian: the first word of a 64-bit one) and
+  // treats a value outside [0, num_slots) as a bad slot: the load reads slot
+  // 0 instead and the item is poisoned.  A 64-bit index whose high word is
+  // not zero is outside the pool too; the prologue checks those words.
+  const bool kv64 = p.kv_idx64 != 0, ocl64 = p.ocl_idx64 != 0;
+  const uint32_t nslots = (uint32_t)p.num_slots;
+  const int kvw = kv64 ? 8 : 4, oclw = ocl64 ? 8 : 4;
+  const unsigned char* kvi = reinterpret_cast<const unsigned char*>(p.kv_indices) + (int64_t)kv0 * kvw;
+  // key j >= P's index at ocl_rel + j * oclw
+  const unsigned char* ocl_rel =
+      reinterpret_cast<const unsigned char*>(p.out_cache_loc) + ((int64_t)q0 - P) * oclw;
+  auto idx_ptr = [&](int j) { return j < P ? kvi + (uint32_t)j * kvw : ocl_rel + (uint32_t)j * oclw; };
+  auto load_slot = [&](int j) -> uint32_t { return *reinterpret_cast<const uint32_t*>(idx_ptr(j)); };
+
+  // ---- the fused KV save: with kv_new, every item whose key range holds
+  // tree keys first stores its request's draft rows into the pool at
+  // out_cache_loc (16 bytes per thread), so its own gathers read them; the
+  // items of a request store the same bytes, and the barrier that ends the
+  // prologue orders a workgroup's stores before its loads.  Rows whose slot
+  // lies outside the pool are not stored (their keys are bad slots).
+  if (p.kv_new && key1 > P) {
+    const int units = T * kRowUnits;
+    for (int u = tid; u < units; u += kPartialThreads) {
+      const int t = u / kRowUnits, c = u % kRowUnits;
+      const int64_t slot = load_index(p.out_cache_loc, (int64_t)q0 + t, ocl64);
+      if (slot < 0 || slot >= p.num_slots) continue;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(p.kv_new + ((int64_t)q0 + t) * p.kv_new_stride_tok + 8 * c);
+      *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.kv_pool) + slot * p.kv_row_stride + 8 * c) = v;
+    }
+  }
+
+  // ---- per-item checks and records (off the tile loop)
+  if (p.kv_new && key1 > P) __syncthreads();   // orders the saved rows before this workgroup's gathers
+  bool out_of_pool = false;
+  bool hidden = false;
+  if ((p.flags & MLA_VERIFY_FLAG_CHECK_PREFIX_MASK) && key0 < P) {
+    // full-row masks: every prefix column of the range must be nonzero for
+    // every node of the request, or the item is poisoned
+    const int len = min(key1, P) - key0;
+    const int64_t cells = (int64_t)T * len;
+    bool h = false;
+    for (int64_t c = tid; c < cells; c += kPartialThreads) {
+      const int i = (int)(c / len), j = key0 + (int)(c % len);
+      h |= p.custom_mask[(int64_t)m0 + (int64_t)i * (P + T) + j] == 0;
+    }
+    hidden = __syncthreads_or(h);
+  }
+  if (p.trace && rb == 0) {
+    // the gathered slot of every key of the range, as read (row block 0's
+    // items cover each key once)
+    for (int j = key0 + tid; j < key1; j += kPartialThreads) {
+      const int64_t raw = j < P ? load_index(p.kv_indices, (int64_t)kv0 + j, kv64)
+                                : load_index(p.out_cache_loc, (int64_t)q0 + (j - P), ocl64);
+      p.trace[(int64_t)kv0 + q0 + j] = raw;
+    }
+  }
+
+  // ---- slot blocks of kIdxKeys keys in LDS (double buffered) ----
+  // The score waves copy the raw index words of block b straight into LDS,
+  // lane = key, with the tile loads.  Keys past the range end re-read the
+  // range's last index.
   auto issue_idx = [&](int blk) {
     const int j = min(key0 + blk * kIdxKeys + 64 * wave + lane, key1 - 1);
-    dma4(kslots + j, lds_addr(&s_idx[blk & 1][64 * wave]));
+    dma4(idx_ptr(j), lds_addr(&s_idx[blk & 1][64 * wave]));
   };
   // ---- direct-to-LDS gather of tile t ----
   // PV wave r fetches the dims [0,512) of keys 4r..4r+3 (one 1 KB load per
@@ -637,45 +734,50 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
   // stalls a wave in the middle of its MFMA stream.  Every key of a tile is a
   // V key of exactly one PV wave, which checks it when it issues its load.
   struct TileSlots {
-    int s;   // score waves: the slot of key 8w + lane / 8 (its rope row);
-             // PV waves: the slot of key 4r + (lane & 3)
+    uint32_t s;   // the raw slot word of this lane's key of a tile: score
+                  // waves key 8w + lane / 8 (its rope row), PV waves key
+                  // 4r + (lane & 3)
+  };
+  auto tile_key = [&](int t) {   // this lane's key of tile t, clamped to the range
+    const int jt = key0 + t * kKeysPerTile;
+    return min(kScore ? jt + 8 * wave + (lane >> 3) : jt + 4 * r + (lane & 3), key1 - 1);
   };
   auto read_slots = [&](int t) {
     const int blk = t / kTilesPerIdx;
-    const int32_t* idx = s_idx[blk & 1] - (key0 + blk * kIdxKeys);
-    const int jt = key0 + t * kKeysPerTile;
-    const int j = score_wave ? min(jt + 8 * wave + (lane >> 3), key1 - 1) : jt + 4 * r + (lane & 3);
-    return TileSlots{idx[j]};
+    return TileSlots{s_idx[blk & 1][tile_key(t) - (key0 + blk * kIdxKeys)]};
   };
+  // the carried slot of a tile key: its pool slot, or kSlotBad outside the pool
+  auto carried = [&](uint32_t v) -> int { return v < nslots ? (int)v : kSlotBad; };
   const unsigned char* pool = reinterpret_cast<const unsigned char*>(p.kv_pool);
   const uint32_t row_bytes = (uint32_t)p.kv_row_stride * 2;
+  auto row_of = [&](int v) {   // latent row of a carried slot; kSlotBad reads slot 0 (the item is poisoned)
+    return pool + (uint64_t)(uint32_t)max(v, 0) * row_bytes;
+  };
   // the loads of a tile one at a time, so that the roles can spread them
   // over their MFMA steps
   auto issue_key = [&](int t, const TileSlots& ts, int i) {
     // one key per load: the slot is wave-uniform, so the row address is
     // formed on the scalar unit
     const int kk = 4 * r + i;
-    const int32_t v = __builtin_amdgcn_readlane(ts.s, i);
-    hidden |= v == kSlotMaskedPrefix;
-    out_of_pool |= v < 0 && v != kSlotMaskedPrefix;
-    const unsigned char* row = pool + (uint64_t)(uint32_t)max(v, 0) * row_bytes;
-    dma16_row(row, (uint32_t)(lane ^ vswz(kk)) * 16, lds_addr(s_v + (t % kStages) * kVSlotBytes + kk * kVStride));
+    const int v = carried((uint32_t)__builtin_amdgcn_readlane((int)ts.s, i));
+    out_of_pool |= v == kSlotBad;
+    dma16_row(row_of(v), (uint32_t)(lane ^ vswz(kk)) * 16, lds_addr(s_v + (t % kStages) * kVSlotBytes + kk * kVStride));
   };
   auto issue_rope = [&](int t, const TileSlots& ts) {
     const int kk = 8 * wave + (lane >> 3);
-    const unsigned char* row = pool + (uint64_t)(uint32_t)max(ts.s, 0) * row_bytes;
     const int unit = (lane & 7) ^ rswz(kk);
-    dma16(row + 2 * kDv + unit * 16, lds_addr(s_r + (t % kRopeSlots) * kRopeSlotBytes + (8 * wave) * 128));
+    const int v = carried(ts.s);
+    dma16(row_of(v) + 2 * kDv + unit * 16, lds_addr(s_r + (t % kRopeSlots) * kRopeSlotBytes + (8 * wave) * 128));
   };
   auto issue = [&](int t, const TileSlots& ts) {
-    if (score_wave) {
+    if (kScore) {
       issue_rope(t, ts);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) issue_key(t, ts, i);
     }
   };
-  const int loads_per_tile = score_wave ? 1 : 4;
+  const int loads_per_tile = kScore ? 1 : 4;
 
   // The two roles run separate loops with the same barrier sequence: one
   // barrier A(i) at the top of each iteration i = 0..ntiles.  Iteration i:
@@ -687,15 +789,15 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
   // i + 1.  Tile i + 2 goes to the V and rope
   // slots of tile i - 1, free since A(i); its slots were read from LDS in
   // iteration i - 1.
-  // Index block b lands before tile 8b - 5 (issued after tile 8b - 6), and
+  // Slot block b lands before tile 8b - 5 (issued after tile 8b - 6), and
   // is first read with the slots of tile 8b in iteration 8b - 3; its buffer
   // was last read in iteration 8b - 12.  The waits below count tile loads
   // only: index loads in flight behind a tile make them wait a little longer,
   // never less.
   TileSlots next_slots{};
-  // The slots of tiles 0..2 come straight from the staged list (the same
-  // values, clamped to the range's last key, that the LDS blocks hold), so
-  // the first gathers wait for one load instead of the first slot block and a
+  // The slots of tiles 0..2 come straight from the index buffers (the same
+  // keys, clamped to the range's last one, that the LDS blocks hold), so the
+  // first gathers wait for one load instead of the first slot block and a
   // barrier.  The first LDS slot read (tile 3, iteration 0) follows A(0),
   // by which every score wave's first index load has landed.  Loads the
   // compiler issued (queries, these slots) are older than the tile loads, so
@@ -705,9 +807,7 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
       if (t >= ntiles) break;
-      const int jt = key0 + t * kKeysPerTile;
-      const int j = min(score_wave ? jt + 8 * wave + (lane >> 3) : jt + 4 * r + (lane & 3), key1 - 1);
-      pre[t] = TileSlots{kslots[j]};
+      pre[t] = TileSlots{load_slot(tile_key(t))};
     }
   };
   auto prologue = [&]() {
@@ -720,33 +820,61 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
     if (i + 1 < ntiles) wait_vm_barrier(loads_per_tile);
     else wait_vm_barrier(0);
   };
-  // what iteration i issues after A(i): tile i + 2, index block i / 8 + 1
-  // (score waves, every 8th iteration) and the slots of tile i + 3
+  // what iteration i issues after A(i): tile i + 2, the raw words of slot
+  // block i / 8 + 1 (score waves, every 8th iteration) and the slots of tile
+  // i + 3
   auto after_a = [&](int i) {
     if (i + 2 < ntiles) issue(i + 2, next_slots);
-    if (score_wave && i % kTilesPerIdx == 0 && i + kTilesPerIdx < ntiles) issue_idx(i / kTilesPerIdx + 1);
+    if (kScore && i % kTilesPerIdx == 0 && i + kTilesPerIdx < ntiles) issue_idx(i / kTilesPerIdx + 1);
     if (i + 3 < ntiles) next_slots = read_slots(i + 3);
   };
 
-  if (score_wave) {
+
+  if constexpr (kScore) {
     // ---- score waves: query rows 16r + n; rows are (node, head), heads fastest
     const bool row_ok = r_local < nrows;
     const bool s_active = r < nrt;
     // the first slot block is on its way while the queries load
     if (ntiles > 0) issue_idx(0);
+    // a 64-bit slot must have a zero high word: wave 0 copies those of the
+    // item's tree keys (node = lane) into LDS now and checks them after the
+    // tile loop, whose waits have seen the copy land
+    const bool tree_hi = ocl64 && key1 > P;
+    const bool hi_lane = wave == 0 && P + lane >= key0 && P + lane < key1;
+    if (tree_hi && wave == 0 && hi_lane) dma4(ocl_rel + (uint32_t)(P + lane) * 8 + 4, lds_addr(&s_tree_hi[0]));
     load_pre();
     bf16x8 qf[kDqk / 32];
-    uint64_t anc;
+    uint64_t anc = 0;
     {
       const int rr = row0 + r_local;
-      const int tok = q0 + rr / H, head = rr % H;
+      const int node = rr / H, head = rr % H;
+      const int tok = q0 + node;
       const uint16_t* qrow = p.q + (int64_t)tok * p.q_stride_tok + (int64_t)head * p.q_stride_head;
 #pragma unroll
       for (int ks = 0; ks < kDqk / 32; ++ks) {
         u32x4 v = row_ok ? *reinterpret_cast<const u32x4*>(qrow + ks * 32 + g * 8) : u32x4{0u, 0u, 0u, 0u};
         qf[ks] = __builtin_bit_cast(bf16x8, v);
       }
-      anc = row_ok ? p.anc[tok] : 0ull;
+      if (key1 > P) {
+        // tree word of the row's node ("The Capture-Safe Kernel", Decision
+        // 5): bit k = its custom_mask entry for tree node k (T x T blocks, or
+        // the tree columns of full rows).  Lane group g reads entries
+        // 16g..16g+15 of the row; the four groups' pieces are joined across
+        // lanes.
+        const bool full = (p.flags & MLA_VERIFY_FLAG_MASK_FULL_ROWS) != 0;
+        const uint8_t* mrow = p.custom_mask + (int64_t)m0 + (full ? P : 0) + (int64_t)node * (full ? P + T : T);
+        uint32_t bits = 0;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int kk = 16 * g + k;
+          if (row_ok && kk < T && mrow[kk] != 0) bits |= 1u << k;
+        }
+        const uint32_t lo = group_or(g == 0 ? bits : g == 1 ? bits << 16 : 0u);
+        const uint32_t hi = group_or(g == 2 ? bits : g == 3 ? bits << 16 : 0u);
+        anc = ((uint64_t)hi << 32) | lo;
+        // recorded once per node (its head-0 row) for inspection
+        if (g == 0 && row_ok && head == 0) p.anc[tok] = anc;
+      }
     }
     float m_run = -INFINITY, l_run = 0.f;       // softmax state of this lane's row
     //   K for S^T (A operand): key 16kt + n, unit 4ks + g (ks < 16) ->
@@ -764,8 +892,10 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
     for (int bf = 0; bf < 2; ++bf) {
       s_p[bf][r][0][lane] = bf16x8{};
       s_p[bf][r][1][lane] = bf16x8{};
-      if (lane == 0) reinterpret_cast<uint8_t*>(&s_rescale[bf])[r] = 0;
     }
+    if (lane == 0)
+#pragma unroll
+      for (int bf = 0; bf < 3; ++bf) reinterpret_cast<uint8_t*>(&s_rescale[bf])[r] = 0;
     prologue();
 
     for (int i = 0; i <= ntiles; ++i) {
@@ -856,15 +986,25 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
       l_run += group_sum(rs);
       s_p[i & 1][r][0][lane] = phi;
       s_p[i & 1][r][1][lane] = plo;
-      if (any_need && g == 0) s_alpha[i & 1][n][r] = alpha;
-      if (lane == 0) reinterpret_cast<uint8_t*>(&s_rescale[i & 1])[r] = any_need;
+      // the rescale flags and factors of tile i, read by the PV waves in
+      // iterations i + 1 and i + 2 (triple buffered: rewritten in i + 3)
+      if (any_need && g == 0) s_alpha[i % 3][n][r] = alpha;
+      if (lane == 0) reinterpret_cast<uint8_t*>(&s_rescale[i % 3])[r] = any_need;
     }
+    if (tree_hi && hi_lane) out_of_pool |= s_tree_hi[lane] != 0u;
+    if (kv64) {
+      // the high words of the range's 64-bit prefix indices
+      for (int j = key0 + tid; j < min(key1, P); j += kWaves * 64)
+        out_of_pool |= *reinterpret_cast<const uint32_t*>(kvi + (uint32_t)j * 8 + 4) != 0u;
+    }
+    // a poisoned item (a slot outside the pool, or a prefix key a checked
+    // full-row mask hides) gives its rows l = NaN; its bits go to this
+    // workgroup's error slot, which the merge launch folds into the header
     out_of_pool = __syncthreads_or(out_of_pool);
-    hidden = __syncthreads_or(hidden);
     const bool poison = out_of_pool || hidden;
-    if (tid == 0 && poison)
-      atomicOr(&p.hdr->err, (out_of_pool ? (uint32_t)MLA_VERIFY_DEVERR_SLOT_RANGE : 0u) |
-                                (hidden ? (uint32_t)MLA_VERIFY_DEVERR_MASK_PREFIX : 0u));
+    if (tid == 0)
+      errbits |= (out_of_pool ? (uint32_t)MLA_VERIFY_DEVERR_SLOT_RANGE : 0u) |
+                 (hidden ? (uint32_t)MLA_VERIFY_DEVERR_MASK_PREFIX : 0u);
     if (row_ok && g == 0) {
       float* pm = p.part_ml + ((size_t)item * kRowsPerItem + r_local) * 2;
       pm[0] = m_run;
@@ -881,29 +1021,37 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
     //   V^T (A operand, transposed read): lane s = 4k + j of group g points at
     //   key 4g + k (and 16 + 4g + k), dims 64r + 16dt + 4j, i.e. unit
     //   8r + 2dt + (j >> 1), byte 8 (j & 1)
-    int v_lo[kDtPerWave];
+    //   The unit index is (8r + h) + 2dt where 8r + h has bits 1-2 clear, so
+    //   the swizzled unit of dim tile dt is that of dim tile 0 with 2dt
+    //   xored in: dim tile dt sits at byte v_lo0 ^ (dt << 5) of the slot.  The
+    //   slots start at multiples of 128 bytes, so the xor can be applied to
+    //   the whole LDS address of the current slot; one register holds the
+    //   offsets of all four dim tiles.
+    int v_lo0;
     {
       const int v_key = 4 * g + (n >> 2);
-#pragma unroll
-      for (int dt = 0; dt < kDtPerWave; ++dt)
-        v_lo[dt] = v_key * kVStride + (n & 1) * 8 + ((((kDvPerWave / 8) * r + 2 * dt + ((n >> 1) & 1)) ^ vswz(v_key)) << 4);
+      v_lo0 = v_key * kVStride + (n & 1) * 8 + ((((kDvPerWave / 8) * r + ((n >> 1) & 1)) ^ vswz(v_key)) << 4);
     }
+    static_assert(kDvPerWave / 8 == 8 && kDtPerWave == 4 && kVSlotBytes % 128 == 0,
+                  "dim tile dt only flips bits 5-6 of the byte offset");
     load_pre();
     prologue();
     // The PV waves run two tiles behind the score waves: iteration i
     // multiplies tile i - 2 with operands that are all in registers by then
-    // (P(i - 2) and its rescale factors, read in iteration i - 1; V^T(i - 2),
-    // read in iteration i - 2), and meanwhile reads P(i - 1) and V^T(i).
+    // (P(i - 2) and its rescale flags, read in iteration i - 1; V^T(i - 2),
+    // read in iteration i - 2), and meanwhile reads P(i - 1) and V^T(i).  A
+    // row tile's rescale factors are read from LDS only when its flag is set
+    // (rarely), so no register holds them.
     // vt[s][dt] is the A operand for dims 64r + 16dt, keys kappa(g, 0..7), of
     // the tile with parity s.
     bf16x8 vt[2][kDtPerWave];
     bf16x8 ph[kWaves], pl[kWaves];
-    uint32_t resc = 0;
-    f32x4 alpha4 = f32x4{1.f, 1.f, 1.f, 1.f};
+    uint32_t resc = 0;   // rescale flags of the tile read last (wave-uniform: a scalar register)
     auto v_operand = [&](const unsigned char* vslot, int dt) -> bf16x8 {
-      const unsigned char* vb = vslot + v_lo[dt];
-      const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MLAV_LDS(i16x4, vb));
-      const i16x4 vc = __builtin_amdgcn_ds_read_tr16_b64_v4i16(MLAV_LDS(i16x4, vb + 16 * kVStride));
+      const uint32_t vb = (lds_addr(vslot) + (uint32_t)v_lo0) ^ (uint32_t)(dt << 5);
+      typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+      const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)vb);
+      const i16x4 vc = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(vb + 16 * kVStride));
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vc, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     auto read_p = [&](int t, int rt) {   // P(t) of row tile rt
@@ -915,15 +1063,16 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
     // two V^T register sets are addressed statically
     // PV of the last tile, in the iteration that reads its P (ntiles): its
     // V^T is in register set sv ^ 1 (read in the iteration before), its P and
-    // rescale factors were loaded in this iteration.  No iteration follows
+    // rescale flags were loaded in this iteration.  No iteration follows
     // only to drain the two-tile lag.
     auto final_pv = [&](auto parity) {
       constexpr int sv = decltype(parity)::value;
+      const int ab = (ntiles - 1) % 3;
 #pragma unroll
       for (int rt = 0; rt < kWaves; ++rt) {
         if (rt < kRowTilesMax) {
           if ((resc >> (8 * rt)) & 0xffu) {
-            const float alpha = alpha4[rt];
+            const float alpha = s_alpha[ab][n][rt];
 #pragma unroll
             for (int dt = 0; dt < kDtPerWave; ++dt) o[dt][rt] *= alpha;
           }
@@ -949,8 +1098,7 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
           for (int dt = 0; dt < kDtPerWave; ++dt) vt[sv][dt] = v_operand(vslot, dt);
         }
         if (p_next) {
-          resc = s_rescale[(i - 1) & 1];
-          alpha4 = s_alpha[(i - 1) & 1][n];
+          resc = uni(s_rescale[(i - 1) % 3]);
 #pragma unroll
           for (int rt = 0; rt < kWaves; ++rt) read_p(i - 1, rt);
         }
@@ -961,11 +1109,8 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
       const bool more_dma = i + 2 < ntiles;
       const bool more_slots = i + 3 < ntiles;
       const uint32_t resc_cur = resc;
-      const f32x4 alpha_cur = alpha4;
-      if (p_next) {
-        resc = s_rescale[(i - 1) & 1];
-        alpha4 = s_alpha[(i - 1) & 1][n];
-      }
+      const int ab = (i - 2) % 3;                  // tile i - 2's factors
+      if (p_next) resc = uni(s_rescale[(i - 1) % 3]);
       // PV of tile i - 2, one row tile at a time (row tiles without rows
       // carry P = 0, so there are no branches but the rare rescale; row tiles
       // past kRowTilesMax are left out at compile time); each P operand, once
@@ -975,7 +1120,7 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
       for (int rt = 0; rt < kWaves; ++rt) {
         if (rt < kRowTilesMax) {
           if ((resc_cur >> (8 * rt)) & 0xffu) {
-            const float alpha = alpha_cur[rt];
+            const float alpha = s_alpha[ab][n][rt];
 #pragma unroll
             for (int dt = 0; dt < kDtPerWave; ++dt) o[dt][rt] *= alpha;
           }
@@ -1018,8 +1163,15 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
       for (int dt = 0; dt < kDtPerWave; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * g) = o[dt][rt];
     }
     out_of_pool = __syncthreads_or(out_of_pool);
-    hidden = __syncthreads_or(hidden);
   }
+  };
+  const int n_run = min(n_mine, kMaxItemsPerWg);
+  if (wave < kWaves) {
+    for (int mi = 0; mi < n_run; ++mi) run_item(mi, std::true_type{});
+  } else {
+    for (int mi = 0; mi < n_run; ++mi) run_item(mi, std::false_type{});
+  }
+  if (tid == 0) p.errs[bid] = (int32_t)errbits;
 }
 
 // ---------------------------------------------------------------------------
@@ -1033,23 +1185,50 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
 // request's key ranges kMergeUnroll at a time.  Wave s of a row takes its
 // ranges c = s, s + w, ... (lane = 8 of the 512 dims), kMergeUnroll per pass
 // with all their loads in flight, and folds them into a running (m, l, O);
-// the w wave results are combined the same way through LDS.  A row waits
-// for about three memory round trips (header, plan entry, partials).
-// Workgroups past the last row exit at once.
+// the w wave results are combined the same way through LDS.  A row waits for
+// two memory round trips: the header together with the token entries of the
+// four possible row mappings, then the partials.  Workgroups past the last
+// row exit at once.
+// Besides, workgroup 0 folds the split-partial workgroups' error slots into
+// the header's error word.
 // ---------------------------------------------------------------------------
 constexpr int kMergeUnroll = 8;
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(KernelParams p) {
   constexpr int kMW = kMergeThreads / 64;
   __shared__ f32x4 s_acc[kMW][2][64];
   __shared__ float s_m[kMW], s_l[kMW];
+  __shared__ uint32_t s_err;
   const WsHeader* hdr = p.hdr;
-  const uint32_t err = hdr->err;
-  const int total_q = hdr->total_q;
-  const int most = hdr->max_chunks;
   const int H = p.num_heads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int wpr = 1;   // waves per row
-  while (wpr < kMW && wpr * kMergeUnroll < most) wpr <<= 1;
+  const uint32_t err = hdr->err_meta;
+  const int total_q = hdr->total_q;
+  const int most = hdr->max_chunks;
+  // the token entry of this wave's row under each mapping w = 1, 2, 4, 8,
+  // loaded beside the header (clamped to the region; used only when live)
+  i32x4 tk_w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int row_k = (int)blockIdx.x * (kMW >> k) + (wave >> k);
+    const int t_k = min(row_k / H, p.max_q_tokens - 1);
+    tk_w[k] = *reinterpret_cast<const i32x4*>(p.tok + 4 * (size_t)t_k);
+  }
+  if (blockIdx.x == 0) {
+    // every device error bit of the call: the metadata checks and each
+    // split-partial workgroup's slot
+    if (tid == 0) s_err = err;
+    __syncthreads();
+    uint32_t e = 0;
+    for (int w = tid; w < p.partial_grid; w += kMergeThreads) e |= (uint32_t)p.errs[w];
+    if (e) atomicOr(&s_err, e);
+    __syncthreads();
+    if (tid == 0) p.hdr->err = s_err;
+  }
+  int lw = 0, wpr = 1;   // waves per row = 2^lw
+  while (wpr < kMW && wpr * kMergeUnroll < most) {
+    wpr <<= 1;
+    ++lw;
+  }
   const int rows_per_wg = kMW / wpr;
   const int row = blockIdx.x * rows_per_wg + wave / wpr;
   const int sub = wave % wpr;
@@ -1067,8 +1246,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(KernelParams p) {
     }
     return;
   }
-  i32x4 tk = i32x4{0, 0, 0, 0};   // q0, item0, row blocks, chunks
-  if (live) tk = *reinterpret_cast<const i32x4*>(p.tok + 4 * (size_t)t);
+  const i32x4 tk = live ? tk_w[lw] : i32x4{0, 0, 0, 0};   // q0, item0, row blocks, chunks
   const int r = (t - tk[0]) * H + h;
   const int rb = r / kRowsPerItem, lr = r % kRowsPerItem;
   const int item0 = tk[1], rbs = tk[2], chunks = live ? tk[3] : 0;
@@ -1284,11 +1462,6 @@ int launch_compact(const KernelParams& p, const int64_t* dst_start, int32_t* err
   if (groups < 1) groups = 1;
   hipLaunchKernelGGL(compact_kernel, dim3((unsigned)groups), dim3(kCompactThreads), 0, (hipStream_t)stream, p,
                      dst_start, error_word);
-  return (int)hipGetLastError();
-}
-
-int launch_meta(const KernelParams& p, const mla_verify_layout_t& lay, void* stream) {
-  hipLaunchKernelGGL(meta_kernel, dim3(lay.meta_grid), dim3(kMetaThreads), 0, (hipStream_t)stream, p);
   return (int)hipGetLastError();
 }
 

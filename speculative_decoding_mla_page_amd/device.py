@@ -1,7 +1,7 @@
 """Torch-side plumbing around the C ABI: device buffers, plan, workspace.
 
 torch provides device memory and the stream; the verify computation itself is
-the library's three HIP launches.  Nothing here computes attention.
+the library's two HIP launches.  Nothing here computes attention.
 """
 from __future__ import annotations
 

@@ -24,7 +24,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert {"mla_verify_plan", "mla_verify_workspace_size", "mla_verify_run"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.mla_verify_abi_version() == 6
+    assert lib.mla_verify_abi_version() == B.ABI_VERSION == 7
 
 
 def test_struct_layout_matches_header(tmp_path):
@@ -66,7 +66,12 @@ def test_plan_layout_arithmetic():
     assert rows in (64, 128) and lay.keys_per_tile == 32 and lay.target_items == 256
     # one partly filled key range per row block, at most
     assert lay.item_capacity == 2 * 256 + (512 * 8 + rows - 1) // rows + 8
-    assert lay.partial_grid % 8 == 0 and lay.item_capacity <= lay.partial_grid < lay.item_capacity + 8
+    # about one split-partial workgroup per target item, in groups of 8, and
+    # enough that none runs more than 4 items
+    assert lay.partial_grid % 8 == 0 and lay.partial_grid >= 256
+    assert (lay.item_capacity + 7) // 8 <= 4 * (lay.partial_grid // 8)
+    wide = B.layout(_plan(target_items=8, num_heads=128, max_q_tokens=512))
+    assert (wide.item_capacity + 7) // 8 <= 4 * (wide.partial_grid // 8) and wide.partial_grid > 8
     assert lay.merge_grid == 512 * 8
     offs = [lay.header_offset, lay.request_offset, lay.anc_offset, lay.items_offset,
             lay.partial_o_offset, lay.partial_ml_offset]
@@ -75,11 +80,14 @@ def test_plan_layout_arithmetic():
     assert lay.total_bytes >= lay.partial_ml_offset + lay.item_capacity * rows * 8
     assert B.workspace_size(p) == lay.total_bytes
     assert lay.trace_offset == 0
-    # staged int32 slots of every key position, after the other regions
-    assert lay.slots_offset % 256 == 0 and lay.slots_offset >= lay.partial_ml_offset
-    assert lay.total_bytes >= lay.slots_offset + (1_480_000 + 512) * 4
-    assert lay.meta_grid == 1 + 256
-    assert B.layout(_plan(max_kv_tokens=1000, max_q_tokens=24)).meta_grid == 2
+    # the small regions after the partials: comparison stats, the merge's
+    # token entries, one error slot per split-partial workgroup (last)
+    assert lay.stats_offset % 256 == 0 and lay.stats_offset >= lay.partial_ml_offset + lay.item_capacity * rows * 8
+    assert lay.tokens_offset % 256 == 0 and lay.tokens_offset >= lay.stats_offset + ctypes.sizeof(B.CompareStats)
+    assert lay.errors_offset % 256 == 0 and lay.errors_offset >= lay.tokens_offset + 512 * 16
+    assert lay.total_bytes == lay.errors_offset + (lay.partial_grid * 4 + 255) // 256 * 256
+    # no per-key region without the trace: the workspace does not grow with the prefix bound
+    assert B.layout(_plan(max_kv_tokens=10)).total_bytes == lay.total_bytes
     t = B.layout(_plan(flags=B.FLAG_TRACE_KEYS))
     assert t.trace_offset % 256 == 0 and t.total_bytes >= t.trace_offset + (1_480_000 + 512) * 8
     # explicit target overrides the CU count
@@ -175,7 +183,9 @@ def test_run_rejects_small_or_misaligned_workspace():
         B.ERR_INVALID_ARGUMENT
     assert lib.mla_verify_run(ctypes.byref(p), ctypes.byref(a), None, need, None) == \
         B.ERR_INVALID_ARGUMENT
-    assert lib.mla_verify_run_phase(ctypes.byref(p), ctypes.byref(a), 1 << 44, need, None, 3) == \
+    assert lib.mla_verify_run_phase(ctypes.byref(p), ctypes.byref(a), 1 << 44, need, None, 2) == \
+        B.ERR_INVALID_ARGUMENT
+    assert lib.mla_verify_run_phase(ctypes.byref(p), ctypes.byref(a), 1 << 44, need, None, -1) == \
         B.ERR_INVALID_ARGUMENT
 
 
@@ -198,12 +208,7 @@ def test_status_strings():
 
 
 def test_mask_layout_flags_plan():
-    """Full-row masks and the prefix check are plan options; the stats region follows the slots."""
+    """Full-row masks and the prefix check are plan options that change no region."""
     lay = B.layout(_plan(flags=B.FLAG_MASK_FULL_ROWS | B.FLAG_CHECK_PREFIX_MASK))
-    assert lay.stats_offset % 256 == 0 and lay.stats_offset >= lay.slots_offset + (1_480_000 + 512) * 4
-    assert lay.total_bytes >= lay.stats_offset + ctypes.sizeof(B.CompareStats)
-    # the merge's per-token table comes last
-    assert lay.tokens_offset % 256 == 0 and lay.tokens_offset >= lay.stats_offset + ctypes.sizeof(B.CompareStats)
-    # then the split-partial workgroups' launch entries
-    assert lay.launch_offset % 256 == 0 and lay.launch_offset >= lay.tokens_offset + 512 * 16
-    assert lay.total_bytes == lay.launch_offset + (lay.partial_grid * 32 + 255) // 256 * 256
+    base = B.layout(_plan())
+    assert lay.total_bytes == base.total_bytes and lay.errors_offset == base.errors_offset

@@ -14,7 +14,8 @@ pytestmark = pytest.mark.gpu
 
 
 def _check_metadata(inst, v, rec):
-    """Tree words, gathered keys (trace) and the work-item table, bit for bit."""
+    """Tree words, gathered keys (trace), the work-item table, the request
+    table and the merge's token entries, bit for bit."""
     import torch
     lay = v.layout
     total_q, total_kv = inst.total_q, inst.total_kv
@@ -32,13 +33,6 @@ def _check_metadata(inst, v, rec):
             base = int(inst.kv_indptr[b]) + int(inst.qo_indptr[b])
             keys = rec["keys"][b]
             assert np.array_equal(tr[base:base + len(keys)], keys), f"request {b}"
-    # staged slots: every request's combined key list, -1 where a slot is outside the pool
-    sl = v.region(lay.slots_offset, max(total_kv + total_q, 1), torch.int32).cpu().numpy()
-    for b in range(inst.batch):
-        base = int(inst.kv_indptr[b]) + int(inst.qo_indptr[b])
-        keys = np.asarray(rec["keys"][b], np.int64)
-        want = np.where((keys >= 0) & (keys < inst.num_slots), keys, -1).astype(np.int32)
-        assert np.array_equal(sl[base:base + len(keys)], want), f"staged slots of request {b}"
     items = v.region(lay.items_offset, max(n_items, 1) * 8, torch.int32).cpu().numpy().reshape(-1, 8)
     items = items[:n_items]
     rows_per = lay.rows_per_item
@@ -56,8 +50,8 @@ def _check_metadata(inst, v, rec):
                 assert e[6] == min(rows_per, t_b * inst.num_heads - rb * rows_per)
                 cover[e[3]:e[4]] += 1
             assert np.all(cover == 1), f"request {b} row block {rb} keys not covered exactly once"
-    # the request table, the merge's per-token entries and the split-partial
-    # launch entries agree with the item table
+    # the request table and the merge's per-token entries agree with the
+    # item table
     req = v.region(lay.request_offset, max(inst.batch, 1) * 8, torch.int32).cpu().numpy().reshape(-1, 8)
     chunks = [int(req[b][5]) for b in range(inst.batch)]
     assert int(hdr[5]) == max(chunks + [0]), "max_chunks in the header"
@@ -69,15 +63,9 @@ def _check_metadata(inst, v, rec):
         mine = np.nonzero(items[:, 0] == b)[0]
         if len(mine):
             assert int(mine.min()) == int(req[b][6]) and len(mine) == int(req[b][4]) * chunks[b]
-    launch = v.region(lay.launch_offset, lay.partial_grid * 8, torch.int32).cpu().numpy().reshape(-1, 8)
-    live = launch[launch[:, 0] >= 0]
-    assert sorted(live[:, 0].tolist()) == list(range(n_items)), "every item launched exactly once"
-    for e in live:
-        it = items[e[0]]
-        b = int(it[0])
-        assert e[1:5].tolist() == [int(it[3]), int(it[4]), int(it[5]), int(it[6])]
-        assert e[5:8].tolist() == [int(inst.prefix_lens[b]), int(inst.qo_indptr[b]),
-                                   int(inst.kv_indptr[b]) + int(inst.qo_indptr[b])]
+    # every workgroup's error slot is written (zero on a clean call)
+    errs = v.region(lay.errors_offset, lay.partial_grid, torch.int32).cpu().numpy()
+    assert np.all(errs == 0), "error slots"
 
 
 @pytest.mark.parametrize("name", ["tiny", "p5632_t16", "p23040_t32", "p91136_t32"])
