@@ -50,6 +50,9 @@ extern "C" {
 #define MLA_VERIFY_D_QK 576          /* latent width used by Q.K^T (512 + 64 rope) */
 #define MLA_VERIFY_D_V 512           /* V = latent dims [0, 512) */
 #define MLA_VERIFY_MAX_TREE_NODES 64 /* tree visibility is packed into one 64-bit word */
+/* bytes of the device array mla_verify_run_static uses as its workspace (per GPU, held until the
+   process ends) */
+#define MLA_VERIFY_STATIC_SCRATCH_BYTES (96u << 20)
 
 typedef enum {
   MLA_VERIFY_OK = 0,
@@ -236,6 +239,23 @@ mla_verify_status_t mla_verify_workspace_size(const mla_verify_plan_t* plan, siz
    MLA_VERIFY_ERR_LAUNCH if HIP refuses a launch. */
 mla_verify_status_t mla_verify_run(const mla_verify_plan_t* plan, const mla_verify_args_t* args,
                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* run() without a caller workspace, for callers that cannot allocate device
+   memory (code under hipGraph capture, tight serving loops, harnesses that
+   forbid allocation): the same two launches, with a workspace taken from a
+   device array of MLA_VERIFY_STATIC_SCRATCH_BYTES that the library holds on
+   each GPU it runs on until the process ends.  The array's address on the
+   current device is looked up on the first call with that device current
+   (make that first call outside capture); the stream must belong to the
+   current device.  It calls no hipMalloc / hipFree.  All calls on one GPU
+   share its array: calls that overlap on one GPU race, so serialise them
+   (one stream, or events); the workspace-resident results (header error
+   word, trace) of the last call live in that array, not in caller memory.
+   Returns MLA_VERIFY_ERR_WORKSPACE_TOO_SMALL (before anything is enqueued)
+   when the plan needs a larger workspace, the argument errors of run(), or
+   MLA_VERIFY_ERR_LAUNCH when the array cannot be located or a launch fails. */
+mla_verify_status_t mla_verify_run_static(const mla_verify_plan_t* plan, const mla_verify_args_t* args,
+                                          void* stream);
 
 /* One of run()'s two launches (phase 0 = split partials with the device-side
    plan, 1 = merge), with the same checks; run() == phases 0, 1 in order on

@@ -146,6 +146,8 @@ def lib() -> ctypes.CDLL:
         l.mla_verify_run.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args), ctypes.c_void_p,
                                      ctypes.c_size_t, ctypes.c_void_p]
         l.mla_verify_run.restype = ctypes.c_int
+        l.mla_verify_run_static.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args), ctypes.c_void_p]
+        l.mla_verify_run_static.restype = ctypes.c_int
         l.mla_verify_run_phase.argtypes = [ctypes.POINTER(Plan), ctypes.POINTER(Args),
                                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                            ctypes.c_int32]
@@ -308,6 +310,17 @@ def run(p: Plan, args: Args, workspace, stream=None) -> None:
                               workspace.numel() * workspace.element_size(), _stream(stream))
     if st != OK:
         raise MlaVerifyError(st, "mla_verify_run")
+
+
+def run_static(p: Plan, args: Args, stream=None) -> None:
+    """Enqueue the two launches with the library's static device scratch as
+    the workspace (no allocation by anyone)."""
+    st = lib().mla_verify_run_static(ctypes.byref(p), ctypes.byref(args), _stream(stream))
+    if st != OK:
+        raise MlaVerifyError(st, "mla_verify_run_static")
+
+
+STATIC_SCRATCH_BYTES = 96 << 20
 
 
 def run_phase(p: Plan, args: Args, workspace, phase: int, stream=None) -> None:

@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libmla_verify.so")
 SOURCES = [os.path.join(PKG, "csrc", "mla_verify_api.cpp"),
            os.path.join(PKG, "csrc", "mla_verify_kernels.hip"),
-           os.path.join(PKG, "csrc", "mla_verify_calibrate.hip")]
+           os.path.join(PKG, "csrc", "mla_verify_calibrate.hip"),
+           os.path.join(PKG, "csrc", "mla_verify_noalloc.hip")]
 ARCH = "gfx950"
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared",

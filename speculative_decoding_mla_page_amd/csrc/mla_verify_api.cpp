@@ -116,6 +116,13 @@ KernelParams make_params(const PlanImpl& pl, const mla_verify_args_t* a, void* w
 
 }  // namespace
 
+mla_verify_status_t mlav::check_call(const mla_verify_plan_t* plan, const mla_verify_args_t* args, const void* ws,
+                                     size_t ws_bytes) {
+  const PlanImpl* pl = as_impl(plan);
+  if (!pl) return MLA_VERIFY_ERR_BAD_PLAN;
+  return check_args(*pl, args, ws, ws_bytes);
+}
+
 extern "C" {
 
 int32_t mla_verify_abi_version(void) { return MLA_VERIFY_ABI_VERSION; }

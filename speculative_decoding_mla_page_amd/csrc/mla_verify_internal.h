@@ -109,6 +109,10 @@ struct KernelParams {
   int64_t ref_lse_stride_tok;
 };
 
+// run()'s host-side checks of a plan and its call arguments (no HIP call)
+mla_verify_status_t check_call(const mla_verify_plan_t* plan, const mla_verify_args_t* args, const void* ws,
+                               size_t ws_bytes);
+
 int launch_partial(const KernelParams& p, const mla_verify_layout_t& lay, void* stream);
 int launch_merge(const KernelParams& p, const mla_verify_layout_t& lay, void* stream);
 int launch_compare(const KernelParams& p, const mla_verify_layout_t& lay, void* stream);

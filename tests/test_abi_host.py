@@ -189,6 +189,21 @@ def test_run_rejects_small_or_misaligned_workspace():
         B.ERR_INVALID_ARGUMENT
 
 
+def test_run_static_rejects_before_any_hip_call():
+    """The allocation-free entry point checks the plan size and the arguments
+    on the host first (no GPU needed for these answers)."""
+    lib = B.lib()
+    big = B.plan(B.make_config(128, 64, 4096, 1_000_000, cu_count=256))
+    assert B.workspace_size(big) > B.STATIC_SCRATCH_BYTES
+    assert lib.mla_verify_run_static(ctypes.byref(big), ctypes.byref(_fake_args()), None) == \
+        B.ERR_WORKSPACE_TOO_SMALL
+    assert lib.mla_verify_run_static(ctypes.byref(B.Plan()), None, None) == B.ERR_BAD_PLAN
+    p = _plan(max_kv_tokens=100_000)
+    assert B.workspace_size(p) <= B.STATIC_SCRATCH_BYTES
+    assert lib.mla_verify_run_static(ctypes.byref(p), ctypes.byref(_fake_args(q=0)), None) == \
+        B.ERR_INVALID_ARGUMENT
+
+
 def test_calibrate_mfma_rejects_bad_arguments_before_launch():
     lib = B.lib()
     assert lib.mla_verify_calibrate_mfma(0, 1, 1 << 44, None) == B.ERR_INVALID_ARGUMENT
