@@ -554,6 +554,16 @@ __device__ __forceinline__ void dma4(const void* addr, uint32_t lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" :: "v"(addr), "{m0}"(lds) : "memory");
 }
 
+// A wave-uniform LDS byte offset the compiler cannot see through.  The tile
+// loops form their per-iteration LDS addresses from such offsets, so that no
+// address becomes an induction register that lives across the whole item:
+// such registers get spilled around the item's prologue and reloaded before
+// the loop, and the wait for a reload that the compiler places at its first
+// use inside the loop waits for every tile load in flight, every iteration.
+__device__ __forceinline__ uint32_t opaque_s(uint32_t v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
 constexpr int kKRing = 8;                  // K operand reads in flight ahead of the S MFMAs
 constexpr int kDvPerWave = kDv / kPVWaves;   // 64 dims of O per PV wave
 constexpr int kDtPerWave = kDvPerWave / 16;
@@ -905,8 +915,8 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
         continue;
       }
       const bool more = i + 2 < ntiles;
-      const unsigned char* vslot = s_v + (i % kStages) * kVSlotBytes;
-      const unsigned char* rslot = s_r + (i % kRopeSlots) * kRopeSlotBytes;
+      const unsigned char* vslot = s_v + opaque_s((uint32_t)(i % kStages) * kVSlotBytes);
+      const unsigned char* rslot = s_r + opaque_s((uint32_t)(i % kRopeSlots) * kRopeSlotBytes);
       const int jt = key0 + i * kKeysPerTile;
       // S^T = K . Q^T: 32 keys x 16 rows, K-dim 576.  The two 16-key halves
       // alternate, so the two independent accumulator chains can issue back
@@ -988,7 +998,9 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
       s_p[i & 1][r][1][lane] = plo;
       // the rescale flags and factors of tile i, read by the PV waves in
       // iterations i + 1 and i + 2 (triple buffered: rewritten in i + 3)
-      if (any_need && g == 0) s_alpha[i % 3][n][r] = alpha;
+      if (any_need && g == 0)
+        *reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(&s_alpha[0][n]) + 4 * r +
+                                  opaque_s((uint32_t)(i % 3) * sizeof(s_alpha[0]))) = alpha;
       if (lane == 0) reinterpret_cast<uint8_t*>(&s_rescale[i % 3])[r] = any_need;
     }
     if (tree_hi && hi_lane) out_of_pool |= s_tree_hi[lane] != 0u;
@@ -1089,7 +1101,7 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
     auto pv_iteration = [&](int i, auto parity) {
       constexpr int sv = decltype(parity)::value;   // = i & 1: V^T(i - 2) in, V^T(i) out
       barrier_a(i);
-      const unsigned char* vslot = s_v + (i % kStages) * kVSlotBytes;
+      const unsigned char* vslot = s_v + opaque_s((uint32_t)(i % kStages) * kVSlotBytes);
       const bool v_next = i < ntiles;              // V^T(i) to read
       const bool p_next = i >= 1 && i <= ntiles;   // P(i - 1) to read
       if (i < 2) {
