@@ -159,7 +159,9 @@ typedef struct {
  *                 aligned, stride a multiple of 8.
  * A row that sees no key (P_b = 0 and an all-zero mask row) gets out = 0 and
  * lse = -inf.  Key order within a request is the prefix, then the tree nodes;
- * a slot listed twice is two keys.  Scores are sm_scale * (q . k).
+ * a slot listed twice is two keys.  Scores are sm_scale * (q . k), sm_scale
+ * finite and positive (the softmax scale; anything else is an invalid
+ * argument).
  */
 typedef struct {
   int32_t batch_size;          /* B, 0..max_batch (host value, fixed at capture) */

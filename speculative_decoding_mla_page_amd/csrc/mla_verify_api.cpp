@@ -30,7 +30,7 @@ mla_verify_status_t check_args(const PlanImpl& pl, const mla_verify_args_t* a, c
   if (!a) return MLA_VERIFY_ERR_INVALID_ARGUMENT;
   const mla_verify_config_t& c = pl.cfg;
   if (a->batch_size < 0 || a->batch_size > c.max_batch) return MLA_VERIFY_ERR_INVALID_ARGUMENT;
-  if (!isfinite(a->sm_scale)) return MLA_VERIFY_ERR_INVALID_ARGUMENT;
+  if (!isfinite(a->sm_scale) || !(a->sm_scale > 0.f)) return MLA_VERIFY_ERR_INVALID_ARGUMENT;
   if (!a->q || !a->kv_pool || !a->qo_indptr || !a->kv_indptr || !a->kv_indices ||
       !a->out_cache_loc || !a->custom_mask || !a->mask_indptr || !a->out)
     return MLA_VERIFY_ERR_INVALID_ARGUMENT;

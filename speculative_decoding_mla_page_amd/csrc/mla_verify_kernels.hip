@@ -32,6 +32,7 @@
 namespace mlav {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
@@ -949,25 +950,26 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
         __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_s_setprio(0);
-      // scores in base-2 units; mask the range tail and invisible tree keys
+      // mask the range tail and invisible tree keys (raw scores: the scale,
+      // positive, is applied to the row max and inside the exponent)
       const bool need_mask = jt + kKeysPerTile > min(P, key1);
-      float mx = -INFINITY;
+      if (need_mask) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float v = sacc[kt][q] * p.sm_scale_log2;
-          if (need_mask) {
+          for (int q = 0; q < 4; ++q) {
             const int j = jt + 16 * kt + 4 * g + q;
             bool vis = j < key1;
             if (j >= P) vis = vis && ((anc >> (j - P)) & 1ull);
-            v = vis ? v : -INFINITY;
+            sacc[kt][q] = vis ? sacc[kt][q] : -INFINITY;
           }
-          sacc[kt][q] = v;
-          mx = fmaxf(mx, v);
         }
       }
-      mx = group_max(mx);
+      // the tile max in base-2 units: scaling by a positive factor commutes
+      // with the max, rounding included
+      float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
+                       fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+      mx = group_max(mx) * p.sm_scale_log2;
       // lazy rescale: move a row's reference max only when the tile max
       // exceeds it by more than 2^kRescaleSlack (then p <= 2^8 stays safe)
       const bool need = mx > m_run + kRescaleSlack;
@@ -980,22 +982,28 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
         m_run = m_new;
       }
       const float m_use = m_run == -INFINITY ? 0.f : m_run;
-      float rs = 0.f;
-      bf16x8 phi, plo;
+      // p = 2^(scale s - m) and its split into bf16 hi + lo: hi = p rounded
+      // to bf16, lo = p - hi (exact in fp32) rounded to bf16, so hi + lo
+      // carries p to about 2^-17.  Pairs are converted together, and hi is
+      // widened back from the packed pair.
+      float pv[8];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int k = 0; k < 8; ++k) pv[k] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[k >> 2][k & 3], p.sm_scale_log2, -m_use));
+      const float rs = ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+      u32x4 hi4, lo4;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float pv = __builtin_amdgcn_exp2f(sacc[kt][q] - m_use);
-          rs += pv;
-          const __bf16 h = (__bf16)pv;
-          phi[kt * 4 + q] = h;
-          plo[kt * 4 + q] = (__bf16)(pv - (float)h);
-        }
+      for (int k = 0; k < 4; ++k) {
+        const bf16x2 hp = {(__bf16)pv[2 * k], (__bf16)pv[2 * k + 1]};
+        const uint32_t hb = __builtin_bit_cast(uint32_t, hp);
+        hi4[k] = hb;
+        const float l0 = pv[2 * k] - __builtin_bit_cast(float, hb << 16);
+        const float l1 = pv[2 * k + 1] - __builtin_bit_cast(float, hb & 0xffff0000u);
+        const bf16x2 lp = {(__bf16)l0, (__bf16)l1};
+        lo4[k] = __builtin_bit_cast(uint32_t, lp);
       }
       l_run += group_sum(rs);
-      s_p[i & 1][r][0][lane] = phi;
-      s_p[i & 1][r][1][lane] = plo;
+      s_p[i & 1][r][0][lane] = __builtin_bit_cast(bf16x8, hi4);
+      s_p[i & 1][r][1][lane] = __builtin_bit_cast(bf16x8, lo4);
       // the rescale flags and factors of tile i, read by the PV waves in
       // iterations i + 1 and i + 2 (triple buffered: rewritten in i + 3)
       if (any_need && g == 0)

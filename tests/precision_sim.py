@@ -10,7 +10,8 @@ the fp32 p; O += P . V accumulated in fp32, with P in one of these forms:
 
   fp32       P as computed (the simulator's own floor)
   bf16       P rounded to bf16 (one bf16 MFMA)
-  bf16x2     P = hi + lo, hi = bf16(p), lo = bf16(p - hi) (two bf16 MFMAs; the kernel)
+  bf16x2     P = hi + lo, hi = bf16(p), lo = bf16(p - hi) (two bf16 MFMAs)
+  bf16x2t    the same with hi = p cut to its top 16 bits (the kernel)
   fp16       P and V rounded to fp16 (one fp16 MFMA; V's bf16 values convert exactly
              unless they fall outside fp16's normal range)
   bf16+e4m3  hi as bf16, lo scaled by 2^9, rounded to OCP fp8 e4m3 (saturating), against V in
@@ -31,7 +32,7 @@ import numpy as np
 
 from oracle import mla_verify_ref as R
 
-SCHEMES = ("fp32", "bf16", "bf16x2", "fp16", "bf16+e4m3")
+SCHEMES = ("fp32", "bf16", "bf16x2", "bf16x2t", "fp16", "bf16+e4m3")
 LOG2E = 1.4426950408889634
 
 
@@ -55,6 +56,12 @@ def to_e4m3(x: np.ndarray) -> np.ndarray:
     q = np.round(a / step) * step          # numpy rounds half to even
     q = np.minimum(q, 448.0)
     return (np.sign(x) * q).astype(np.float32)
+
+
+def trunc_bf16(x: np.ndarray) -> np.ndarray:
+    """float32 cut to its top 16 bits (a bf16 value, rounded toward zero)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return (u & np.uint32(0xFFFF0000)).view(np.float32)
 
 
 def simulate(inst, scheme: str, tile: int = 32, slack: float = 8.0):
@@ -110,6 +117,11 @@ def simulate(inst, scheme: str, tile: int = 32, slack: float = 8.0):
                 o += to_bf16(p) @ vt
             elif scheme == "bf16x2":
                 hi = to_bf16(p)
+                lo = to_bf16(p - hi)
+                o += hi @ vt
+                o += lo @ vt
+            elif scheme == "bf16x2t":
+                hi = trunc_bf16(p)
                 lo = to_bf16(p - hi)
                 o += hi @ vt
                 o += lo @ vt

@@ -163,6 +163,8 @@ def _fake_args(**kw):
     (dict(batch_size=9), B.ERR_INVALID_ARGUMENT),
     (dict(batch_size=-1), B.ERR_INVALID_ARGUMENT),
     (dict(sm_scale=float("nan")), B.ERR_INVALID_ARGUMENT),
+    (dict(sm_scale=0.0), B.ERR_INVALID_ARGUMENT),
+    (dict(sm_scale=-0.07), B.ERR_INVALID_ARGUMENT),
 ])
 def test_run_rejects_bad_arguments_before_launch(kw, status):
     p = _plan()

@@ -33,7 +33,7 @@ def test_to_e4m3_matches_torch_in_range_and_saturates():
 
 
 def test_scheme_verdicts_on_tiny():
-    """Only the split hi + lo bf16 form of P (and fp32 itself) clears the gate:
+    """Only the split hi + lo bf16 forms of P (and fp32 itself) clear the gate:
     one bf16 rounding of P, fp16 P and V, and a bf16 + e4m3 split all miss the
     2-ULP share on the tiny 4-node chain workload."""
     inst = gen.config("tiny")
@@ -41,4 +41,5 @@ def test_scheme_verdicts_on_tiny():
                                                  inst.kv_indices, inst.out_cache_loc, inst.custom_mask,
                                                  inst.mask_indptr, inst.num_heads, inst.sm_scale)
     verdict = {s: P.passes(P.gate(*P.simulate(inst, s), ref_out, ref_lse)) for s in P.SCHEMES}
-    assert verdict == {"fp32": True, "bf16": False, "bf16x2": True, "fp16": False, "bf16+e4m3": False}
+    assert verdict == {"fp32": True, "bf16": False, "bf16x2": True, "bf16x2t": True, "fp16": False,
+                       "bf16+e4m3": False}
