@@ -111,16 +111,25 @@ __device__ __forceinline__ long long div_up(long long a, long long b) {
 // kv_indptr[b] (Decision 2), the checks behind the metadata error bits, and
 // its query rows (node, head), heads fastest, cut into 64-row blocks.  Each
 // request's combined key range [0, P_b + T_b) is cut into ranges of one
-// length shared by all requests, rounded to 32 keys and at least 128.  Five
-// candidate lengths cut the total work W = sum_b rowblocks_b (P_b + T_b) into
-// about target_items pieces, or m target_items - sum_b rowblocks_b pieces for
-// m = 1..4 (each row block adds at most one partly filled range); the one
-// with the least modelled time - rounds of target_items workgroups x (tiles
-// per range + the per-item cost, about kItemTiles tiles) - among those whose
-// items fit the plan is taken.  Work items are numbered request by request,
-// then key range, then row block.
+// length shared by all requests, rounded to 32 keys and at least 128.
+// Twenty candidate lengths cut the total work W = sum_b rowblocks_b (P_b +
+// T_b) into m target_items - f R pieces, for m = 1..4 rounds, R = sum_b
+// rowblocks_b and f = 1, 3/4, 1/2, 1/4, 0 (each row block adds at most one
+// partly filled range: f = 1 leaves room for all of them, smaller f packs the
+// rounds fuller); the one with the least modelled time - rounds of
+// target_items workgroups x (tiles per range + the per-item cost, about
+// kItemTiles tiles) - among those whose items fit the plan is taken (m = 1,
+// f = 0, when none fits: the call is flagged).  Work items are numbered
+// request by request, then key range, then row block.
 // ---------------------------------------------------------------------------
-constexpr int kCands = 5;
+constexpr int kCands = 20;
+// candidate k: the pieces m target_items - f R with m = 1 + k / 5 and
+// f = (4 - k % 5) / 4
+__device__ __forceinline__ long long cand_slots(int k, int target, int rowblocks) {
+  const long long s = (long long)(1 + k / 5) * target - ((long long)rowblocks * (4 - k % 5)) / 4;
+  return s < 1 ? 1 : s;
+}
+constexpr int kFallbackCand = 4;   // m = 1, f = 0: about target_items pieces
 constexpr long long kItemTiles = 6;
 constexpr int kPlanWaves = kPartialThreads / 64;
 struct PlanShared {
@@ -130,6 +139,9 @@ struct PlanShared {
   int w_items[kPlanWaves][kCands];
   int w_scan[kPlanWaves];
   int w_most[kPlanWaves];
+  float w_cost[kPlanWaves];            // per wave: its best candidate's modelled time, length, index
+  int w_c[kPlanWaves];
+  int w_k[kPlanWaves];
   int total_q;
   // the plan
   uint32_t err;
@@ -192,13 +204,16 @@ __device__ __forceinline__ uint32_t dpp_or(uint32_t v) {
 // kMaxBatch of them stay in 32 bits (a count that large never fits a plan)
 constexpr int kItemsCap = 1 << 20;
 
-// The plan for at most 64 requests, by one wave (lane b = request b): one
-// global round trip for the indptrs, then DPP reductions; no barrier.  The
-// total work is summed in float, which is exact enough to pick a range
-// length and, being the same sum in every workgroup, gives every workgroup
-// the same plan.
+// The plan for at most 64 requests (lane b = request b), run by every wave
+// of the workgroup on the same inputs: one global round trip for the
+// indptrs, then DPP reductions; wave 0 writes the tables.  When the
+// candidate lengths have to be timed, the waves share them out and meet at
+// one barrier.  The total work is summed in float, which is exact enough to
+// pick a range length and, being the same sum in every workgroup, gives
+// every workgroup the same plan.
 __device__ void plan_call_wave(const KernelParams& p, int32_t (*req)[8], PlanShared& sp) {
   const int lane = threadIdx.x & 63;
+  const int wv = (int)(threadIdx.x >> 6);
   const int B = p.batch;
   const int H = p.num_heads;
   const bool full_rows = (p.flags & MLA_VERIFY_FLAG_MASK_FULL_ROWS) != 0;
@@ -224,7 +239,7 @@ __device__ void plan_call_wave(const KernelParams& p, int32_t (*req)[8], PlanSha
   const int Tc = T < 0 ? 0 : T, Pc = P < 0 ? 0 : P;
   const int N = Pc + Tc;
   const int rb = (int)(((long long)Tc * H + kRowsPerItem - 1) / kRowsPerItem);
-  if (have) {
+  if (wv == 0 && have) {
     req[lane][RQ_P] = Pc;
     req[lane][RQ_T] = Tc;
     req[lane][RQ_Q0] = q0;
@@ -243,27 +258,57 @@ __device__ void plan_call_wave(const KernelParams& p, int32_t (*req)[8], PlanSha
   auto items_of = [&](int c) {   // this lane's request under range length c
     return rb > 0 ? (int)min((long long)rb * ((N + c - 1) / c), (long long)kItemsCap) : 0;
   };
-  int chunk_sel = 0;
-  float best = -1.f;
-  const float inv_target = 1.f / (float)p.target_items;
+  auto cand_len = [&](int k) {   // candidate k's range length
+    const float per = ceilf(workf / (float)cand_slots(k, p.target_items, rowblocks));
+    const int c = per >= (float)(1 << 30) ? (1 << 30) : ((int)per + kKeysPerTile - 1) / kKeysPerTile * kKeysPerTile;
+    return c < kMinChunkKeys ? kMinChunkKeys : c;
+  };
+  // One round of about target_items ranges (the fallback candidate, the
+  // shortest one-round length) is the best plan whenever its items fit in
+  // one round: every other one-round candidate is longer, and two rounds cost
+  // at least kItemTiles tiles more.  Only otherwise are all candidates timed.
+  int chunk_sel = cand_len(kFallbackCand);
+  const int items_fb = dpp_sum(items_of(chunk_sel));
+  if (items_fb > p.target_items) {   // the same decision in every wave
+    // wave w times candidates w, w + kPlanWaves, ...; modelled time: rounds
+    // of target_items workgroups x (tiles per range + the per-item cost);
+    // float, so that it takes no integer division
+    float best = -1.f;
+    int best_c = 0, best_k = kCands;
+    const float inv_target = 1.f / (float)p.target_items;
+    for (int m = wv; m < kCands; m += kPlanWaves) {
+      const int c = cand_len(m);
+      const int items = dpp_sum(items_of(c));
+      const float rounds = fmaxf(1.f, ceilf((float)items * inv_target));
+      const float cost = items > p.item_capacity ? -1.f : rounds * (float)(c / kKeysPerTile + kItemTiles);
+      if (cost >= 0.f && (best < 0.f || cost < best)) {
+        best = cost;
+        best_c = c;
+        best_k = m;
+      }
+    }
+    if (lane == 0) {
+      sp.w_cost[wv] = best;
+      sp.w_c[wv] = best_c;
+      sp.w_k[wv] = best_k;
+    }
+    __syncthreads();
+    // the least time, the lowest candidate among equals (a serial scan's pick);
+    // none fits: the fallback length stays, and the call is flagged below
+    best = -1.f;
+    best_k = kCands;
 #pragma unroll
-  for (int m = 0; m < kCands; ++m) {
-    float slots = m == 0 ? (float)p.target_items : (float)m * p.target_items - rowblocks;
-    if (slots < 1.f) slots = 1.f;
-    const float per = ceilf(workf / slots);
-    int c = per >= (float)(1 << 30) ? (1 << 30) : ((int)per + kKeysPerTile - 1) / kKeysPerTile * kKeysPerTile;
-    if (c < kMinChunkKeys) c = kMinChunkKeys;
-    const int items = dpp_sum(items_of(c));
-    // modelled time: rounds of target_items workgroups x (tiles per range +
-    // the per-item cost); float, so that it takes no integer division
-    const float rounds = fmaxf(1.f, ceilf((float)items * inv_target));
-    const float cost = items > p.item_capacity ? -1.f : rounds * (float)(c / kKeysPerTile + kItemTiles);
-    if (m == 0) chunk_sel = c;   // none fits: cand[0], flagged below
-    if (cost >= 0.f && (best < 0.f || cost < best)) {
-      best = cost;
-      chunk_sel = c;
+    for (int w = 0; w < kPlanWaves; ++w) {
+      const float cw = sp.w_cost[w];
+      const int kw = sp.w_k[w];
+      if (cw >= 0.f && (best < 0.f || cw < best || (cw == best && kw < best_k))) {
+        best = cw;
+        best_k = kw;
+        chunk_sel = sp.w_c[w];
+      }
     }
   }
+  if (wv != 0) return;   // wave 0 writes the tables
   // each request's first item: an inclusive scan of the item counts over the
   // lanes (DPP: shifts inside each 16-lane row, then the last lane of a row
   // broadcast into the rows after it), less the lane's own count
@@ -299,7 +344,7 @@ __device__ void plan_call_wave(const KernelParams& p, int32_t (*req)[8], PlanSha
 // plan fields and req hold the plan.
 __device__ void plan_call(const KernelParams& p, int32_t (*req)[8], PlanShared& sp) {
   if (p.batch <= 64) {
-    if (threadIdx.x < 64) plan_call_wave(p, req, sp);
+    plan_call_wave(p, req, sp);
     __syncthreads();
     return;
   }
@@ -367,8 +412,7 @@ __device__ void plan_call(const KernelParams& p, int32_t (*req)[8], PlanShared& 
   int cand[kCands];
 #pragma unroll
   for (int m = 0; m < kCands; ++m) {
-    long long slots = m == 0 ? (long long)p.target_items : (long long)m * p.target_items - rowblocks;
-    if (slots < 1) slots = 1;
+    const long long slots = cand_slots(m, p.target_items, rowblocks);
     const long long per_item = div_up(work, slots);
     long long c = ((per_item + kKeysPerTile - 1) / kKeysPerTile) * kKeysPerTile;
     if (c < kMinChunkKeys) c = kMinChunkKeys;
@@ -376,7 +420,7 @@ __device__ void plan_call(const KernelParams& p, int32_t (*req)[8], PlanShared& 
     cand[m] = (int)c;
   }
   {
-    int mine[kCands] = {0, 0, 0, 0, 0};
+    int mine[kCands] = {};
     for (int b = tid; b < B; b += kThreads)
 #pragma unroll
       for (int m = 0; m < kCands; ++m) mine[m] += items_of(b, cand[m]);
@@ -389,8 +433,9 @@ __device__ void plan_call(const KernelParams& p, int32_t (*req)[8], PlanShared& 
   __syncthreads();
   // the candidate with the least modelled time: rounds of target_items
   // workgroups x (tiles per range + the per-item cost, about kItemTiles
-  // tiles), among those whose items fit the plan; none fits: cand[0], flagged
-  int chunk_sel = cand[0];
+  // tiles), among those whose items fit the plan; none fits: the fallback
+  // candidate, flagged
+  int chunk_sel = cand[kFallbackCand];
   {
     long long best = -1;
 #pragma unroll
