@@ -147,6 +147,29 @@ def test_mixed_batch_edges():
     assert_gate(out, lse, ref_out, ref_lse, label="mixed")
 
 
+@pytest.mark.parametrize("label,batch,tree_hi,heads", [
+    ("batch100", 100, 16, 8),      # more requests than one wave holds: the multi-wave plan
+    ("decode300", 300, 1, 16),     # 300 one-node requests: several rounds, every candidate timed
+])
+def test_large_batch_plans(label, batch, tree_hi, heads):
+    """Batches of more than 64 requests take the plan's multi-wave path (every
+    thread takes requests, wave reductions and barriers); the second case has
+    more items than one round holds, so every candidate length is timed."""
+    need_gpu()
+    rng = np.random.default_rng(400 + batch)
+    prefixes = [int(x) for x in rng.integers(0, 3000, batch)]
+    trees = [int(x) for x in rng.integers(1, tree_hi + 1, batch)]
+    prefixes[3] = 0                             # one request with no prefix
+    inst = gen.make_instance(prefixes, trees, heads, num_slots=1 << 19, seed=401 + batch)
+    say(f"{label}: B={batch} keys={sum(prefixes) + sum(trees)} H={heads}")
+    from speculative_decoding_mla_page_amd import binding as B
+    out, lse, v, _ = run_gpu(inst, flags=B.FLAG_TRACE_KEYS, max_tree_nodes=max(trees))
+    ref_out, ref_lse, rec = oracle(inst)
+    _check_metadata(inst, v, rec)
+    assert_rows_finite(out, lse, label=label)
+    assert_gate(out, lse, ref_out, ref_lse, label=label)
+
+
 def test_index_dtypes_strides_and_padded_rows():
     """int64 kv_indices, int32 out_cache_loc, strided q/out, pool rows of 640."""
     need_gpu()
