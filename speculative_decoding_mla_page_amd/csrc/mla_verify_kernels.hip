@@ -1063,7 +1063,7 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
         out_of_pool |= *reinterpret_cast<const uint32_t*>(kvi + (uint32_t)j * 8 + 4) != 0u;
     }
     // a poisoned item (a slot outside the pool, or a prefix key a checked
-    // full-row mask hides) gives its rows l = NaN; its bits go to this
+    // full-row mask hides) gives its rows m = +inf, l = NaN; its bits go to this
     // workgroup's error slot, which the merge launch folds into the header
     out_of_pool = __syncthreads_or(out_of_pool);
     const bool poison = out_of_pool || hidden;
@@ -1072,7 +1072,9 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
                  (hidden ? (uint32_t)MLA_VERIFY_DEVERR_MASK_PREFIX : 0u);
     if (row_ok && g == 0) {
       float* pm = p.part_ml + ((size_t)item * kRowsPerItem + r_local) * 2;
-      pm[0] = m_run;
+      // a poisoned item: m = +inf, l = NaN (the merge then gives NaN rows
+      // even when none of the item's scores was finite)
+      pm[0] = poison ? INFINITY : m_run;
       pm[1] = poison ? NAN : l_run;
     }
   } else {
@@ -1318,7 +1320,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(KernelParams p) {
   auto item_of = [&](int c) { return (size_t)(item0 + c * rbs + rb) * kRowsPerItem + lr; };
 
   // fold weights 2^(m_c - M) into a running (M, L, acc); a range with no
-  // visible key (m_c = -inf) adds nothing
+  // visible key (m_c = -inf) adds nothing.  A poisoned range carries m_c =
+  // +inf and l_c = NaN: it takes the running max to +inf, its weight is
+  // 2^(inf - inf) = NaN, and every later rescale is NaN too, so the row
+  // comes out NaN.
   float M = -INFINITY, L = 0.f;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   for (int c0 = sub; c0 < chunks; c0 += wpr * kMergeUnroll) {

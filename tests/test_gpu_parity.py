@@ -263,6 +263,32 @@ def test_slot_out_of_range_sets_error_and_nan_rows():
     assert_gate(out, lse, ref_out, ref_lse, tokens=[4, 5, 6], label="other request")
 
 
+def test_ranges_of_bad_slots_only_give_nan_rows():
+    """Every prefix index of request 0 outside the pool: its all-prefix key
+    ranges read slot 0, a NaN row here, so all their scores are NaN and their
+    reference max stays -inf.  The poison must still reach the merged rows."""
+    torch = need_gpu()
+    from speculative_decoding_mla_page_amd import binding as B
+    from speculative_decoding_mla_page_amd.device import DeviceInputs, Verifier
+    inst = gen.make_instance([700, 200], [4, 3], 8, num_slots=2048, seed=103)
+    used = set(np.asarray(inst.kv_indices).tolist()) | set(np.asarray(inst.out_cache_loc).tolist())
+    assert 0 not in used
+    inst.kv_indices = np.asarray(inst.kv_indices).copy()
+    inst.kv_indices[:700] = 2048 + 5
+    say("ranges of bad slots only")
+    di = DeviceInputs(inst)
+    di.pool[0] = -1                          # bf16 NaN bits
+    v = Verifier.for_inputs(di)
+    out, lse = di.alloc_outputs()
+    v(di, out, lse)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    assert v.error_word() & B.DEVERR_SLOT_RANGE
+    assert np.isnan(out[:4]).all() and np.isnan(lse[:4]).all()
+    ref_out, ref_lse, _ = oracle(inst, tokens=[4, 5, 6])
+    assert_gate(out, lse, ref_out, ref_lse, tokens=[4, 5, 6], label="other request")
+
+
 @pytest.mark.parametrize("what", ["mask_indptr", "tree_size", "kv_indptr"])
 def test_bad_metadata_sets_error_and_nan(what):
     need_gpu()
