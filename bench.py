@@ -374,14 +374,26 @@ def main():
         for _ in range(args.steps):
             B.run(ver.plan, a, ver.workspace, sp)
         ve[1].record(stream)
+        # the same calls through the contiguous-prefix fast path
+        ver_c = Verifier.for_inputs(di, max_tree_nodes=max(1, max(int(t) for t in inst.tree_sizes)),
+                                    flags=B.FLAG_CONTIGUOUS_PREFIX)
+        a_c = ver_c.args(di, out, lse)
+        for _ in range(5):
+            B.run(ver_c.plan, a_c, ver_c.workspace, sp)
+        vc = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        vc[0].record(stream)
+        for _ in range(args.steps):
+            B.run(ver_c.plan, a_c, ver_c.workspace, sp)
+        vc[1].record(stream)
         torch.cuda.synchronize()
-        if int(err.item()) != 0 or ver.error_word() != 0:
+        if int(err.item()) != 0 or ver.error_word() != 0 or ver_c.error_word() != 0:
             raise RuntimeError("compaction reported an error")
         compaction = {"first_call_us": ce2[0].elapsed_time(ce2[1]) * 1e3,
                       "us_per_call": float(np.median([ce2[k].elapsed_time(ce2[k + 1])
                                                       for k in range(args.compact_calls)]) * 1e3),
                       "rows": int(di.total_kv), "bytes_moved": int(di.total_kv) * 1152 * 2,
-                      "verify_us_per_call_after": ve[0].elapsed_time(ve[1]) * 1e3 / args.steps}
+                      "verify_us_per_call_after": ve[0].elapsed_time(ve[1]) * 1e3 / args.steps,
+                      "verify_us_per_call_contiguous_prefix": vc[0].elapsed_time(vc[1]) * 1e3 / args.steps}
 
     # reference numbers: the same call checked for the device error word
     if ver.error_word() != 0:

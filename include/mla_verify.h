@@ -81,7 +81,20 @@ enum {
      nonzero; a zero marks the keys it covers, the work items that gather them
      write NaN rows and set MLA_VERIFY_DEVERR_MASK_PREFIX.  Costs one mask byte
      read per (tree node, prefix key). */
-  MLA_VERIFY_FLAG_CHECK_PREFIX_MASK = 4u
+  MLA_VERIFY_FLAG_CHECK_PREFIX_MASK = 4u,
+  /* contiguous-prefix fast path for a compacted pool (the defragmentation
+     plan of "The Integration Chasm", The Decision: Adapt the Kernel, Not the
+     System): the caller guarantees that every request's prefix indices are
+     consecutive, kv_indices[kv_indptr[b] + j] = kv_indices[kv_indptr[b]] + j
+     for j < P_b (as mla_verify_compact leaves them).  The kernel then reads
+     each request's first prefix index and gathers prefix key j from slot
+     base_b + j; of the other prefix indices it reads only the last few
+     (fewer than 64) before the tree keys.  A base outside the pool (or
+     base_b + j past it) poisons the work items that gather those keys (NaN
+     rows, MLA_VERIFY_DEVERR_SLOT_RANGE).  Prefixes that break the guarantee
+     are not detected: their rows come from base_b + j (those last few from
+     their own indices).  Tree keys (out_cache_loc) are read as usual. */
+  MLA_VERIFY_FLAG_CONTIGUOUS_PREFIX = 8u
 };
 
 /* bits of the device error word (first uint32 of the workspace) */

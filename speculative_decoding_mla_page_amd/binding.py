@@ -20,6 +20,7 @@ I32, I64 = 0, 1
 FLAG_TRACE_KEYS = 1
 FLAG_MASK_FULL_ROWS = 2
 FLAG_CHECK_PREFIX_MASK = 4
+FLAG_CONTIGUOUS_PREFIX = 8
 
 OK = 0
 ERR_INVALID_ARGUMENT = 1

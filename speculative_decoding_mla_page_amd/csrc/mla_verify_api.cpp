@@ -149,7 +149,7 @@ mla_verify_status_t mla_verify_plan(const mla_verify_config_t* cfg, mla_verify_p
       (c.out_cache_loc_dtype != MLA_VERIFY_I32 && c.out_cache_loc_dtype != MLA_VERIFY_I64))
     return MLA_VERIFY_ERR_INVALID_ARGUMENT;
   if (c.flags & ~(uint32_t)(MLA_VERIFY_FLAG_TRACE_KEYS | MLA_VERIFY_FLAG_MASK_FULL_ROWS |
-                            MLA_VERIFY_FLAG_CHECK_PREFIX_MASK))
+                            MLA_VERIFY_FLAG_CHECK_PREFIX_MASK | MLA_VERIFY_FLAG_CONTIGUOUS_PREFIX))
     return MLA_VERIFY_ERR_INVALID_ARGUMENT;
   // the prefix check reads the prefix columns of full mask rows
   if ((c.flags & MLA_VERIFY_FLAG_CHECK_PREFIX_MASK) && !(c.flags & MLA_VERIFY_FLAG_MASK_FULL_ROWS))

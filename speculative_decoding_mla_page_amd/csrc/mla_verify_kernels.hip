@@ -621,7 +621,7 @@ static_assert(kTilesPerIdx >= 5, "an index block is loaded five tiles ahead of i
 // ceil(min(64, max_tree_nodes x H) / 16); an instantiation for fewer than four
 // (decode: one node per request) leaves out the PV MFMAs and P reads of row
 // tiles that can hold no row.
-template <int kRowTilesMax>
+template <int kRowTilesMax, bool kContig>
 __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParams p) {
   __shared__ __attribute__((aligned(128))) unsigned char s_v[kStages * kVSlotBytes];
   __shared__ __attribute__((aligned(16))) unsigned char s_r[kRopeSlots * kRopeSlotBytes];
@@ -727,6 +727,23 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
       reinterpret_cast<const unsigned char*>(p.out_cache_loc) + ((int64_t)q0 - P) * oclw;
   auto idx_ptr = [&](int j) { return j < P ? kvi + (uint32_t)j * kvw : ocl_rel + (uint32_t)j * oclw; };
   auto load_slot = [&](int j) -> uint32_t { return *reinterpret_cast<const uint32_t*>(idx_ptr(j)); };
+  // ---- contiguous-prefix fast path (a compacted prefix, "The Integration
+  // Chasm", The Decision: Adapt the Kernel, Not the System): prefix key j is
+  // slot cb + j with cb = kv_indices[kv0].  The only other prefix indices
+  // read are those of the 64-key share that reaches the tree keys (fewer than
+  // 64 keys right before them), which a compacted prefix holds as cb + j too.
+  // A base outside the pool (or a 64-bit one with a nonzero high word) is
+  // replaced by num_slots, so that every prefix key of the request is outside
+  // the pool; cb + j stays below 2^32 (both terms are below 2^31).
+  // The base is loaded where it is used (the prologues), not kept live
+  // through the item.
+  const bool contig = kContig && P > 0;
+  auto contig_base = [&]() -> uint32_t {
+    const uint32_t lo = *reinterpret_cast<const uint32_t*>(kvi);
+    const uint32_t hi = kv64 ? *reinterpret_cast<const uint32_t*>(kvi + 4) : 0u;
+    return (hi == 0u && lo < nslots) ? lo : nslots;
+  };
+  uint32_t cb = nslots;   // the score waves' copy, for the slot blocks
 
   // ---- the fused KV save: with kv_new, every item whose key range holds
   // tree keys first stores its request's draft rows into the pool at
@@ -762,10 +779,10 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
     hidden = __syncthreads_or(h);
   }
   if (p.trace && rb == 0) {
-    // the gathered slot of every key of the range, as read (row block 0's
-    // items cover each key once)
+    // the gathered slot of every key of the range, as read (computed on the
+    // fast path; row block 0's items cover each key once)
     for (int j = key0 + tid; j < key1; j += kPartialThreads) {
-      const int64_t raw = j < P ? load_index(p.kv_indices, (int64_t)kv0 + j, kv64)
+      const int64_t raw = j < P ? (contig ? (int64_t)contig_base() + j : load_index(p.kv_indices, (int64_t)kv0 + j, kv64))
                                 : load_index(p.out_cache_loc, (int64_t)q0 + (j - P), ocl64);
       p.trace[(int64_t)kv0 + q0 + j] = raw;
     }
@@ -775,8 +792,16 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
   // The score waves copy the raw index words of block b straight into LDS,
   // lane = key, with the tile loads.  Keys past the range end re-read the
   // range's last index.
+  // On the fast path a wave whose 64 keys are all prefix keys writes their
+  // slot words itself (an LDS store lands no later than the copy would); the
+  // one share per request that reaches the tree keys still copies its words.
   auto issue_idx = [&](int blk) {
-    const int j = min(key0 + blk * kIdxKeys + 64 * wave + lane, key1 - 1);
+    const int c0 = key0 + blk * kIdxKeys + 64 * wave;
+    const int j = min(c0 + lane, key1 - 1);
+    if (contig && min(c0 + 63, key1 - 1) < P) {
+      s_idx[blk & 1][64 * wave + lane] = cb + (uint32_t)j;
+      return;
+    }
     dma4(idx_ptr(j), lds_addr(&s_idx[blk & 1][64 * wave]));
   };
   // ---- direct-to-LDS gather of tile t ----
@@ -800,7 +825,20 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
   };
   auto read_slots = [&](int t) {
     const int blk = t / kTilesPerIdx;
-    return TileSlots{s_idx[blk & 1][tile_key(t) - (key0 + blk * kIdxKeys)]};
+    if constexpr (kContig) {
+      // A slot block holds a word at every position (keys past the range end
+      // repeat the last key's), so a tile key's position needs no clamp; the
+      // lane index is formed here, since a lane offset kept from before the
+      // loop was spilled around this instantiation's item set-up, and its
+      // reload's wait inside the loop would also wait for every tile load in
+      // flight.
+      int ln;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+      const int pos = (t % kTilesPerIdx) * kKeysPerTile + (kScore ? 8 * wave + (ln >> 3) : 4 * r + (ln & 3));
+      return TileSlots{s_idx[blk & 1][pos]};
+    } else {
+      return TileSlots{s_idx[blk & 1][tile_key(t) - (key0 + blk * kIdxKeys)]};
+    }
   };
   // the carried slot of a tile key: its pool slot, or kSlotBad outside the pool
   auto carried = [&](uint32_t v) -> int { return v < nslots ? (int)v : kSlotBad; };
@@ -860,10 +898,13 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
   // the tile waits only ever wait longer for them.
   TileSlots pre[3] = {};
   auto load_pre = [&]() {
+    const uint32_t cbp = contig ? contig_base() : 0u;
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
       if (t >= ntiles) break;
-      pre[t] = TileSlots{load_slot(tile_key(t))};
+      // fast path: a tile of prefix keys only has computed slots
+      if (contig && key0 + (t + 1) * kKeysPerTile <= P) pre[t] = TileSlots{cbp + (uint32_t)tile_key(t)};
+      else pre[t] = TileSlots{load_slot(tile_key(t))};
     }
   };
   auto prologue = [&]() {
@@ -891,6 +932,7 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
     const bool row_ok = r_local < nrows;
     const bool s_active = r < nrt;
     // the first slot block is on its way while the queries load
+    if (contig) cb = contig_base();
     if (ntiles > 0) issue_idx(0);
     // a 64-bit slot must have a zero high word: wave 0 copies those of the
     // item's tree keys (node = lane) into LDS now and checks them after the
@@ -1057,7 +1099,7 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
       if (lane == 0) reinterpret_cast<uint8_t*>(&s_rescale[i % 3])[r] = any_need;
     }
     if (tree_hi && hi_lane) out_of_pool |= s_tree_hi[lane] != 0u;
-    if (kv64) {
+    if (kv64 && !contig) {
       // the high words of the range's 64-bit prefix indices
       for (int j = key0 + tid; j < min(key1, P); j += kWaves * 64)
         out_of_pool |= *reinterpret_cast<const uint32_t*>(kvi + (uint32_t)j * 8 + 4) != 0u;
@@ -1535,16 +1577,27 @@ int launch_compact(const KernelParams& p, const int64_t* dst_start, int32_t* err
   return (int)hipGetLastError();
 }
 
+template <bool kContig>
+static void launch_partial_tiles(const KernelParams& p, const mla_verify_layout_t& lay, int tiles, void* stream) {
+  if (tiles <= 1)
+    hipLaunchKernelGGL((partial_kernel<1, kContig>), dim3(lay.partial_grid), dim3(kPartialThreads), 0,
+                       (hipStream_t)stream, p);
+  else if (tiles == 2)
+    hipLaunchKernelGGL((partial_kernel<2, kContig>), dim3(lay.partial_grid), dim3(kPartialThreads), 0,
+                       (hipStream_t)stream, p);
+  else
+    hipLaunchKernelGGL((partial_kernel<kWaves, kContig>), dim3(lay.partial_grid), dim3(kPartialThreads), 0,
+                       (hipStream_t)stream, p);
+}
+
 int launch_partial(const KernelParams& p, const mla_verify_layout_t& lay, void* stream) {
-  // the most rows an item of this plan holds bound its 16-row tiles
+  // the most rows an item of this plan holds bound its 16-row tiles; the
+  // contiguous-prefix fast path is an instantiation of its own, so that the
+  // index path's code is unchanged by it
   const int64_t rows = (int64_t)p.max_tree_nodes * p.num_heads;
   const int tiles = rows >= kRowsPerItem ? kWaves : (int)((rows + 15) / 16);
-  if (tiles <= 1)
-    hipLaunchKernelGGL(partial_kernel<1>, dim3(lay.partial_grid), dim3(kPartialThreads), 0, (hipStream_t)stream, p);
-  else if (tiles == 2)
-    hipLaunchKernelGGL(partial_kernel<2>, dim3(lay.partial_grid), dim3(kPartialThreads), 0, (hipStream_t)stream, p);
-  else
-    hipLaunchKernelGGL(partial_kernel<kWaves>, dim3(lay.partial_grid), dim3(kPartialThreads), 0, (hipStream_t)stream, p);
+  if (p.flags & MLA_VERIFY_FLAG_CONTIGUOUS_PREFIX) launch_partial_tiles<true>(p, lay, tiles, stream);
+  else launch_partial_tiles<false>(p, lay, tiles, stream);
   return (int)hipGetLastError();
 }
 

@@ -229,3 +229,10 @@ def test_mask_layout_flags_plan():
     lay = B.layout(_plan(flags=B.FLAG_MASK_FULL_ROWS | B.FLAG_CHECK_PREFIX_MASK))
     base = B.layout(_plan())
     assert lay.total_bytes == base.total_bytes and lay.errors_offset == base.errors_offset
+
+
+def test_contiguous_prefix_flag_plan():
+    """The contiguous-prefix fast path is a plan option that changes no region."""
+    lay = B.layout(_plan(flags=B.FLAG_CONTIGUOUS_PREFIX))
+    base = B.layout(_plan())
+    assert lay.total_bytes == base.total_bytes and lay.partial_grid == base.partial_grid

@@ -78,3 +78,81 @@ def test_compaction_out_of_pool_destination_is_refused():
     assert ok.sum() == 50
     assert np.array_equal(after[k1:inst.total_kv][ok], dst1[ok])
     assert np.array_equal(after[k1:inst.total_kv][~ok], before[k1:inst.total_kv][~ok])
+
+
+@pytest.mark.parametrize("idx64", [False, True])
+def test_contiguous_prefix_fast_path(idx64):
+    """With MLA_VERIFY_FLAG_CONTIGUOUS_PREFIX on a compacted pool the call
+    gathers prefix key j from kv_indices[kv0] + j: the same rows, so the same
+    bits as the index path, and the prefix indices in the middle of a prefix
+    are never read.  A base outside the pool poisons its request only."""
+    torch = need_gpu()
+    from speculative_decoding_mla_page_amd import binding as B
+    from speculative_decoding_mla_page_amd.device import DeviceInputs, Verifier
+    # prefixes: several slot blocks, none, shorter than a tile share, one
+    # block plus a ragged tail, and one ending inside a 64-key share
+    inst = gen.make_instance([3000, 0, 129, 1700, 40, 700], [16, 3, 7, 5, 2, 9], 8, num_slots=16384, seed=97)
+    say(f"contiguous prefix idx64={idx64}")
+    di = DeviceInputs(inst, kv_indices_dtype=B.I64 if idx64 else B.I32)
+    base = inst.num_slots + 32
+    extra = torch.full((32 + inst.total_kv + 32, di.pool.shape[1]), -1, dtype=di.pool.dtype, device=di.pool.device)
+    di.pool = torch.cat([di.pool, extra])
+    di.num_slots = di.pool.shape[0]
+    flags = B.FLAG_TRACE_KEYS
+    v = Verifier.for_inputs(di, flags=flags)
+    vf = Verifier.for_inputs(di, flags=flags | B.FLAG_CONTIGUOUS_PREFIX)
+    out, lse = di.alloc_outputs()
+    args = v.args(di, out, lse)
+    dst = torch.tensor([base + int(inst.kv_indptr[b]) for b in range(inst.batch)], dtype=torch.int64,
+                       device=di.pool.device)
+    err = torch.zeros(1, dtype=torch.int32, device=di.pool.device)
+    B.compact(v.plan, args, dst, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    n_tr = inst.total_kv + inst.total_q
+
+    def call(ver):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        ver(di, out, lse)
+        torch.cuda.synchronize()
+        tr = ver.region(ver.layout.trace_offset, n_tr, torch.int64).cpu().numpy().copy()
+        return out.cpu().numpy().copy(), lse.cpu().numpy().copy(), tr, ver.error_word()
+
+    o_idx, l_idx, tr_idx, e_idx = call(v)
+    o_fp, l_fp, tr_fp, e_fp = call(vf)
+    assert e_idx == 0 and e_fp == 0
+    assert np.array_equal(tr_fp, tr_idx)
+    assert np.array_equal(o_fp.view(np.uint32), o_idx.view(np.uint32))
+    assert np.array_equal(l_fp.view(np.uint32), l_idx.view(np.uint32))
+    ref_out, ref_lse, _ = oracle(inst)
+    assert_gate(o_fp, l_fp, ref_out, ref_lse, label="contiguous prefix")
+
+    # indices in the middle of request 0's prefix and of request 3's are not
+    # read: scrambling them changes nothing
+    kvp = np.asarray(inst.kv_indptr, dtype=np.int64)
+    saved = di.kv_indices.clone()
+    for b, lo, hi in ((0, 300, 2800), (3, 1, 1500)):
+        n = hi - lo
+        junk = torch.randint(0, inst.num_slots, (n,), dtype=torch.int64, device=di.pool.device)
+        di.kv_indices[int(kvp[b]) + lo:int(kvp[b]) + hi] = junk.to(di.kv_indices.dtype)
+    o_s, l_s, tr_s, e_s = call(vf)
+    assert e_s == 0
+    assert np.array_equal(o_s.view(np.uint32), o_idx.view(np.uint32))
+    assert np.array_equal(l_s.view(np.uint32), l_idx.view(np.uint32))
+    assert np.array_equal(tr_s, tr_idx)
+
+    # a base outside the pool (or, for 64-bit indices, with a high word set)
+    # poisons request 2 alone
+    di.kv_indices.copy_(saved)
+    bad = (1 << 40) + int(dst[2].item()) if idx64 else di.num_slots + 5
+    di.kv_indices[int(kvp[2])] = bad
+    o_b, l_b, _, e_b = call(vf)
+    assert e_b & B.DEVERR_SLOT_RANGE
+    q = np.asarray(inst.qo_indptr, dtype=np.int64)
+    rows2 = slice(int(q[2]), int(q[3]))
+    assert np.isnan(o_b[rows2]).all() and np.isnan(l_b[rows2]).all()
+    keep = np.ones(o_b.shape[0], dtype=bool)
+    keep[rows2] = False
+    assert np.array_equal(o_b[keep].view(np.uint32), o_idx[keep].view(np.uint32))
+    assert np.array_equal(l_b[keep].view(np.uint32), l_idx[keep].view(np.uint32))

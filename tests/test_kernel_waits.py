@@ -83,7 +83,9 @@ def loop_waits(lines, fn_pattern):
 
 def test_no_compiler_vmcnt_wait_in_tile_loops(asm):
     found = loop_waits(asm, "partial_kernel")
-    assert len(found) == 3, sorted(found)   # the <1>, <2> and <4> row-tile instantiations
+    # the <1>, <2> and <4> row-tile instantiations, each with and without the
+    # contiguous-prefix fast path
+    assert len(found) == 6, sorted(found)
     bad = {}
     for name, loops in found.items():
         tile_loops = [lp for lp in loops if lp[1] >= 2 and lp[2]]
