@@ -692,6 +692,14 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   auto run_item = [&](int mi, auto role) {
   constexpr bool kScore = decltype(role)::value;
+  // The thread and lane index, formed anew for every item: what the compiler
+  // derived from them once, before the item loop, did not stay in registers
+  // through it and went to scratch (stores of some 60-96 bytes per lane by
+  // every workgroup, about 11 MB of extra HBM writes per launch).
+  int tid_item = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid_item));
+  const int tid = tid_item;
+  const int lane = tid & 63;
   const int item = uni(s_mine[mi][0]);
   const int b = uni(s_mine[mi][1]), rb = uni(s_mine[mi][2]), chunk_no = uni(s_mine[mi][3]);
   const int P = uni(s_mine[mi][4]), T = uni(s_mine[mi][5]);
@@ -994,6 +1002,11 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
     if (lane == 0)
 #pragma unroll
       for (int bf = 0; bf < 3; ++bf) reinterpret_cast<uint8_t*>(&s_rescale[bf])[r] = 0;
+    // the query loads are waited for here, before the first gathers: left
+    // to the compiler, that wait sat inside the tile loop, where on the
+    // hardware it also waits for every tile load in flight
+#pragma unroll
+    for (int ks = 0; ks < kDqk / 32; ++ks) asm volatile("" :: "v"(qf[ks]));
     prologue();
 
     for (int i = 0; i <= ntiles; ++i) {

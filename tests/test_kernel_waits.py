@@ -94,3 +94,23 @@ def test_no_compiler_vmcnt_wait_in_tile_loops(asm):
             if waits:
                 bad[f"{name} loop {h}"] = waits
     assert not bad, bad
+
+
+def test_no_scratch_in_the_split_partial_kernel(asm):
+    """No instantiation spills to scratch: a spill of per-item values costs
+    stores from every lane of every workgroup (HBM writes) and reloads whose
+    waits the compiler places wherever the value is first used."""
+    sizes = {}
+    cur = None
+    for ln in asm:
+        m = re.match(r"^\s*\.amdhsa_kernel (\S+)", ln)
+        if m:
+            cur = m.group(1)
+            continue
+        m = re.match(r"^\s*\.amdhsa_private_segment_fixed_size (\d+)", ln)
+        if m and cur is not None:
+            sizes[cur] = int(m.group(1))
+            cur = None
+    partial = {k: v for k, v in sizes.items() if "partial_kernel" in k}
+    assert len(partial) == 6, sorted(sizes)
+    assert all(v == 0 for v in partial.values()), partial
