@@ -967,13 +967,22 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
         // the tree columns of full rows).  Lane group g reads entries
         // 16g..16g+15 of the row; the four groups' pieces are joined across
         // lanes.
+        // The sixteen byte loads are unconditional, so that they are all in
+        // flight together (a load under a lane condition got a branch and a
+        // wait of its own each): a row past the item's rows reads node 0's
+        // entries and an entry past T reads entry T - 1, both in the block,
+        // and the conditions are applied to the loaded bytes.
         const bool full = (p.flags & MLA_VERIFY_FLAG_MASK_FULL_ROWS) != 0;
-        const uint8_t* mrow = p.custom_mask + (int64_t)m0 + (full ? P : 0) + (int64_t)node * (full ? P + T : T);
+        const int node_c = row_ok ? node : 0;
+        const uint8_t* mrow = p.custom_mask + (int64_t)m0 + (full ? P : 0) + (int64_t)node_c * (full ? P + T : T);
+        uint8_t mb[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) mb[k] = mrow[min(16 * g + k, T - 1)];
         uint32_t bits = 0;
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
           const int kk = 16 * g + k;
-          if (row_ok && kk < T && mrow[kk] != 0) bits |= 1u << k;
+          if (row_ok && kk < T && mb[k] != 0) bits |= 1u << k;
         }
         const uint32_t lo = group_or(g == 0 ? bits : g == 1 ? bits << 16 : 0u);
         const uint32_t hi = group_or(g == 2 ? bits : g == 3 ? bits << 16 : 0u);
