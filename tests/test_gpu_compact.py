@@ -156,3 +156,65 @@ def test_contiguous_prefix_fast_path(idx64):
     keep[rows2] = False
     assert np.array_equal(o_b[keep].view(np.uint32), o_idx[keep].view(np.uint32))
     assert np.array_equal(l_b[keep].view(np.uint32), l_idx[keep].view(np.uint32))
+
+
+def _fast_path_case(name):
+    """(device instance, oracle instance, DeviceInputs keywords, plan flags) of
+    one fast-path case."""
+    from speculative_decoding_mla_page_amd import binding as B
+    from tests.test_gpu_mask_layout import full_row_instance
+    rng = np.random.default_rng(500)
+    if name in ("decode40", "decode100"):
+        n = 40 if name == "decode40" else 100
+        prefixes = rng.integers(0, 3000, n).tolist()
+        prefixes[3] = 0
+        inst = gen.make_instance(prefixes, [1] * n, 16, num_slots=1 << 19, seed=501 + n)
+        return inst, inst, {}, 0
+    mixed = gen.make_instance([0, 37, 1500, 1, 77, 2600], [3, 0, 16, 1, 5, 32], 8, num_slots=16384, seed=502)
+    if name == "full_rows_checked":
+        return full_row_instance(mixed), mixed, {}, B.FLAG_MASK_FULL_ROWS | B.FLAG_CHECK_PREFIX_MASK
+    if name == "fused_save":
+        return mixed, mixed, {"fused_save": True}, 0
+    if name == "ocl_int32_kv_int64":
+        return mixed, mixed, {"out_cache_loc_dtype": B.I32, "kv_indices_dtype": B.I64}, 0
+    raise ValueError(name)
+
+
+@pytest.mark.parametrize("name", ["decode40", "decode100", "full_rows_checked", "fused_save",
+                                  "ocl_int32_kv_int64"])
+def test_contiguous_prefix_matches_index_path(name):
+    """The fast path gives the index path's bits on a compacted pool, with each
+    plan option and with many requests (the multi-wave plan)."""
+    torch = need_gpu()
+    from speculative_decoding_mla_page_amd import binding as B
+    from speculative_decoding_mla_page_amd.device import DeviceInputs, Verifier
+    inst, ref_inst, dev_kw, flags = _fast_path_case(name)
+    say(f"contiguous prefix vs index path: {name}")
+    di = DeviceInputs(inst, **dev_kw)
+    base = di.num_slots + 32
+    extra = torch.full((32 + inst.total_kv + 32, di.pool.shape[1]), -1, dtype=di.pool.dtype, device=di.pool.device)
+    di.pool = torch.cat([di.pool, extra])
+    di.num_slots = di.pool.shape[0]
+    tn = max(1, max(int(t) for t in inst.tree_sizes))
+    v = Verifier.for_inputs(di, flags=flags, max_tree_nodes=tn)
+    vf = Verifier.for_inputs(di, flags=flags | B.FLAG_CONTIGUOUS_PREFIX, max_tree_nodes=tn)
+    out, lse = di.alloc_outputs()
+    dst = torch.tensor([base + int(inst.kv_indptr[b]) for b in range(inst.batch)], dtype=torch.int64,
+                       device=di.pool.device)
+    err = torch.zeros(1, dtype=torch.int32, device=di.pool.device)
+    B.compact(v.plan, v.args(di, out, lse), dst, err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    res = []
+    for ver in (v, vf):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        ver(di, out, lse)
+        torch.cuda.synchronize()
+        assert ver.error_word() == 0
+        res.append((out.cpu().numpy().copy(), lse.cpu().numpy().copy()))
+    (o_i, l_i), (o_f, l_f) = res
+    assert np.array_equal(o_f.view(np.uint32), o_i.view(np.uint32))
+    assert np.array_equal(l_f.view(np.uint32), l_i.view(np.uint32))
+    ref_out, ref_lse, _ = oracle(ref_inst)
+    assert_gate(o_f, l_f, ref_out, ref_lse, label=f"contiguous prefix {name}")
