@@ -66,11 +66,18 @@ constexpr float kRescaleSlack = 8.f;  // rescale O only when a row max grows by 
 // Row reductions over the four lane groups that hold one query row (lanes
 // n, n+16, n+32, n+48): the gfx950 swaps exchange 16-lane rows (xor 16) and
 // 32-lane halves (xor 32) in the VALU, with no LDS round trip.
-__device__ __forceinline__ float group_max(float v) {
+// The larger of two scores as one v_med3_f32: the median of a, b and pinf,
+// where pinf holds +inf in a register the compiler cannot see into (with a
+// constant +inf the compiler turns the median back into a max).  fmaxf
+// costs an extra v_max per operand, because the compiler quiets each input
+// first: the hardware max does not follow maxnum for signalling NaNs.
+// Scores are finite or -inf; a NaN score only occurs in a poisoned item.
+__device__ __forceinline__ float max_sc(float a, float b, float pinf) { return __builtin_amdgcn_fmed3f(a, b, pinf); }
+__device__ __forceinline__ float group_max(float v, float pinf) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = max_sc(__uint_as_float(a[0]), __uint_as_float(a[1]), pinf);
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return max_sc(__uint_as_float(b[0]), __uint_as_float(b[1]), pinf);
 }
 __device__ __forceinline__ uint32_t group_or(uint32_t v) {
   auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
@@ -992,6 +999,9 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
       }
     }
     float m_run = -INFINITY, l_run = 0.f;       // softmax state of this lane's row
+    float m_use = 0.f;                           // m_run, or 0 while it is -inf
+    float pinf = INFINITY;                       // for max_sc
+    asm volatile("" : "+s"(pinf));
     //   K for S^T (A operand): key 16kt + n, unit 4ks + g (ks < 16) ->
     //   k_lo[ks & 3] + 256 (ks >> 2) + 16 kt * 1024; rope unit 4(ks - 16) + g.
     //   The swizzle only touches the low 4 bits of a unit index, so the rest
@@ -1076,21 +1086,25 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
       }
       // the tile max in base-2 units: scaling by a positive factor commutes
       // with the max, rounding included
-      float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
-                       fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
-      mx = group_max(mx) * p.sm_scale_log2;
+      float mx = max_sc(max_sc(max_sc(sacc[0][0], sacc[0][1], pinf), max_sc(sacc[0][2], sacc[0][3], pinf), pinf),
+                        max_sc(max_sc(sacc[1][0], sacc[1][1], pinf), max_sc(sacc[1][2], sacc[1][3], pinf), pinf),
+                        pinf);
+      mx = group_max(mx, pinf) * p.sm_scale_log2;
       // lazy rescale: move a row's reference max only when the tile max
       // exceeds it by more than 2^kRescaleSlack (then p <= 2^8 stays safe)
       const bool need = mx > m_run + kRescaleSlack;
       const bool any_need = __builtin_amdgcn_ballot_w64(need) != 0;
       float alpha = 1.f;
       if (any_need) {
+        // a branch, not selects: the compiler would otherwise compute this
+        // rare path on every tile
+        asm volatile("");
         const float m_new = need ? mx : m_run;
         alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
         m_run = m_new;
+        m_use = m_run == -INFINITY ? 0.f : m_run;
       }
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;
       // p = 2^(scale s - m) and its split into bf16 hi + lo: hi = p rounded
       // to bf16, lo = p - hi (exact in fp32) rounded to bf16, so hi + lo
       // carries p to about 2^-17.  Pairs are converted together, and hi is
@@ -1103,7 +1117,10 @@ __global__ __launch_bounds__(kPartialThreads, 1) void partial_kernel(KernelParam
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const bf16x2 hp = {(__bf16)pv[2 * k], (__bf16)pv[2 * k + 1]};
-        const uint32_t hb = __builtin_bit_cast(uint32_t, hp);
+        uint32_t hb = __builtin_bit_cast(uint32_t, hp);
+        // the widened halves come from the packed pair (otherwise the
+        // compiler converted the low element a second time)
+        asm volatile("" : "+v"(hb));
         hi4[k] = hb;
         const float l0 = pv[2 * k] - __builtin_bit_cast(float, hb << 16);
         const float l1 = pv[2 * k + 1] - __builtin_bit_cast(float, hb & 0xffff0000u);
