@@ -10,7 +10,15 @@ for bit and leave every output row finite; every tenth replay (and the last)
 is compared with the oracle on all of its nodes.  out, lse and the workspace
 sit between guard bands of a fixed bit pattern that must survive all replays
 (a write past either end of any of them would change it).
+
+The same capture runs a second time with the contiguous-prefix fast path:
+before each replay every request's prefix indices are rewritten as one
+contiguous run from a random base (the pool is fully populated), as a
+compacted pool would hold them.
 """
+import copy
+import functools
+
 import numpy as np
 import pytest
 
@@ -21,6 +29,7 @@ pytestmark = pytest.mark.gpu
 
 N_REPLAYS = 100
 ORACLE_REPLAYS = set(range(0, N_REPLAYS, 10)) | {N_REPLAYS - 1}
+N_REPLAYS_CONTIG = 20
 GUARD_BYTES = 64 * 1024          # each side; a multiple of 256 keeps the workspace aligned
 CANARY = 0x5AC3E11D              # guard word (a NaN-free float bit pattern)
 
@@ -38,6 +47,26 @@ def _fill(static, rep, torch):
     put("custom_mask", rep.custom_mask)
     qf = torch.from_numpy(rep.q.view(np.int16))
     static["q"][:qf.shape[0]].copy_(qf)
+
+
+@functools.lru_cache(maxsize=1)
+def _pool_np():
+    return gen.segmented_pool()
+
+
+def _contiguous(rep, r, num_slots):
+    """The replay with each request's prefix indices one run from a random base."""
+    rng = np.random.default_rng(9000 + r)
+    out = copy.copy(rep)
+    kvi = np.asarray(rep.kv_indices).copy()
+    kvp = np.asarray(rep.kv_indptr)
+    for b in range(len(kvp) - 1):
+        n = int(kvp[b + 1] - kvp[b])
+        if n:
+            base = int(rng.integers(0, num_slots - n))
+            kvi[kvp[b]:kvp[b + 1]] = base + np.arange(n)
+    out.kv_indices = kvi.astype(np.asarray(rep.kv_indices).dtype)
+    return out
 
 
 class Guarded:
@@ -59,16 +88,19 @@ class Guarded:
         return bool((lo == CANARY).all().item()) and bool((hi == CANARY).all().item())
 
 
-def test_graph_capture_replay_segmented():
+@pytest.mark.parametrize("contig", [False, True], ids=["index_path", "contiguous_prefix"])
+def test_graph_capture_replay_segmented(contig):
     torch = need_gpu()
     from speculative_decoding_mla_page_amd import binding as B
     from oracle import mla_verify_ref as R
+    n_replays = N_REPLAYS_CONTIG if contig else N_REPLAYS
+    oracle_replays = ({0, n_replays // 2, n_replays - 1} if contig else ORACLE_REPLAYS)
 
     bounds = gen.SEGMENTED_BOUNDS
     h = gen.SEGMENTED["num_heads"]
     dev = torch.device("cuda")
     say("segmented: building the 2M-slot pool")
-    pool_np = gen.segmented_pool()
+    pool_np = _pool_np()
     pool = torch.from_numpy(pool_np.view(np.int16)).to(dev)
     mq = bounds["max_q_tokens"]
     static = {
@@ -81,7 +113,8 @@ def test_graph_capture_replay_segmented():
         "custom_mask": torch.zeros(mq * bounds["max_tree_nodes"], dtype=torch.uint8, device=dev),
     }
     cfg = B.make_config(h, bounds["max_batch"], mq, bounds["max_kv_tokens"],
-                        max_tree_nodes=bounds["max_tree_nodes"])
+                        max_tree_nodes=bounds["max_tree_nodes"],
+                        flags=B.FLAG_CONTIGUOUS_PREFIX if contig else 0)
     plan = B.plan(cfg)
     ws_bytes = B.workspace_size(plan)
     g_out = Guarded(torch, mq * h * 512 * 4, dev)
@@ -107,7 +140,11 @@ def test_graph_capture_replay_segmented():
     a_graph = args(out_g, lse_g)
     a_eager = args(out_e, lse_e)
 
-    rep0 = gen.segmented_replay(0)
+    def replay(r):
+        rep = gen.segmented_replay(r)
+        return _contiguous(rep, r, pool_np.shape[0]) if contig else rep
+
+    rep0 = replay(0)
     _fill(static, rep0, torch)
     torch.cuda.synchronize()
     say("segmented: eager warm-up, then capture")
@@ -123,8 +160,8 @@ def test_graph_capture_replay_segmented():
     torch.cuda.synchronize()
     assert g_out.intact() and g_lse.intact() and g_ws.intact(), "capture wrote outside its buffers"
 
-    for r in range(N_REPLAYS):
-        rep = rep0 if r == 0 else gen.segmented_replay(r)
+    for r in range(n_replays):
+        rep = rep0 if r == 0 else replay(r)
         _fill(static, rep, torch)
         out_g.fill_(float("nan"))
         g.replay()
@@ -139,7 +176,7 @@ def test_graph_capture_replay_segmented():
         oe = out_e[:rep.total_q].cpu().numpy()
         le = lse_e[:rep.total_q].cpu().numpy()
         assert np.array_equal(og, oe) and np.array_equal(lg, le), f"replay {r} != eager"
-        if r in ORACLE_REPLAYS:
+        if r in oracle_replays:
             say(f"segmented replay {r}: oracle on all {rep.total_q} nodes, P={rep.prefix_lens} "
                 f"T={rep.tree_sizes}")
             ro, rl, _ = R.mla_verify_reference(rep.q, pool_np, rep.qo_indptr, rep.kv_indptr,
