@@ -15,7 +15,10 @@
 //                   unnormalised partial (O, running max, running sum) - the
 //                   KV-split partial of the pages' split-K design ("The
 //                   Integration Chasm", Context: What Came Before; "The
-//                   Capture-Safe Kernel", Decision 3).
+//                   Capture-Safe Kernel", Decision 3).  A second
+//                   instantiation serves compacted pools, taking each prefix
+//                   key's slot as the request's first slot + j instead of
+//                   reading its index.
 //   merge_kernel    combines the partial softmax statistics of each query row
 //                   across its key ranges ("The Capture-Safe Kernel", Decision 4)
 //                   into the normalised output and its log-sum-exp.
