@@ -13,11 +13,11 @@ N_CASES = 12
 MAX_ROW_KEYS = 40_000_000     # bound on sum_b T_b * H * (P_b + T_b), so the oracle takes about a second
 
 
-def draw_case(seed):
+def draw_case(seed, head_choices=(1, 2, 8, 16, 32)):
     """One random case: (instance, DeviceInputs keywords, plan keywords, full_rows)."""
     from speculative_decoding_mla_page_amd import binding as B
     rng = np.random.default_rng(seed)
-    heads = int(rng.choice([1, 2, 8, 16, 32]))
+    heads = int(rng.choice(head_choices))
     batch = int(rng.integers(1, 81))
     while True:
         # prefixes: mostly short, some long, some empty
@@ -43,13 +43,11 @@ def draw_case(seed):
     return inst, dev_kw, plan_kw, full_rows
 
 
-@pytest.mark.parametrize("case", range(N_CASES))
-def test_random_instance(case):
+def _run_case(case, inst, dev_kw, plan_kw, full_rows):
     torch = need_gpu()
     from speculative_decoding_mla_page_amd import binding as B
     from speculative_decoding_mla_page_amd.device import DeviceInputs, Verifier
     from tests.test_gpu_mask_layout import full_row_instance
-    inst, dev_kw, plan_kw, full_rows = draw_case(7000 + case)
     dev_inst = full_row_instance(inst) if full_rows else inst
     say(f"random case {case}: B={inst.batch} H={inst.num_heads} T={list(inst.tree_sizes)[:8]}... "
         f"P_max={max(inst.prefix_lens)} {dev_kw} {plan_kw} full_rows={full_rows}")
@@ -63,3 +61,15 @@ def test_random_instance(case):
     assert v.error_word() == 0
     ref_out, ref_lse, _ = oracle(inst)
     assert_gate(out.cpu().numpy(), lse.cpu().numpy(), ref_out, ref_lse, label=f"random case {case}")
+
+
+@pytest.mark.parametrize("case", range(N_CASES))
+def test_random_instance(case):
+    _run_case(case, *draw_case(7000 + case))
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_random_instance_odd_heads(case):
+    """Head counts that do not divide the 64-row block: a row block ends in
+    the middle of a tree node, and an item's rows span several nodes."""
+    _run_case(100 + case, *draw_case(7100 + case, head_choices=(3, 5, 12, 24, 48, 96)))
