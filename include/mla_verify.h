@@ -57,7 +57,7 @@ extern "C" {
 typedef enum {
   MLA_VERIFY_OK = 0,
   MLA_VERIFY_ERR_INVALID_ARGUMENT = 1, /* null / misaligned pointer, bad size or stride */
-  MLA_VERIFY_ERR_UNSUPPORTED = 2,      /* a configuration this build does not implement */
+  MLA_VERIFY_ERR_UNSUPPORTED = 2,      /* a configuration the library does not implement */
   MLA_VERIFY_ERR_WORKSPACE_TOO_SMALL = 3,
   MLA_VERIFY_ERR_LAUNCH = 4,           /* the HIP runtime refused a launch */
   MLA_VERIFY_ERR_BAD_PLAN = 5          /* plan not produced by mla_verify_plan */
