@@ -147,6 +147,19 @@ int main() {
   b = a;
   b.sm_scale = 1.0f / 0.0f;
   CHECK(mla_verify_run(&plan, &b, wsp, ws, nullptr) == MLA_VERIFY_ERR_INVALID_ARGUMENT);
+  // the contiguous-prefix fast path is a plan option that the launches see
+  {
+    mla_verify_config_t cf = config(8, 8, 512, 1480000);
+    cf.flags = MLA_VERIFY_FLAG_CONTIGUOUS_PREFIX;
+    mla_verify_plan_t pf;
+    CHECK(mla_verify_plan(&cf, &pf) == MLA_VERIFY_OK);
+    size_t wsf = 0;
+    CHECK(mla_verify_workspace_size(&pf, &wsf) == MLA_VERIFY_OK && wsf == ws);
+    CHECK(mla_verify_run(&pf, &a, wsp, wsf, nullptr) == MLA_VERIFY_OK);
+    CHECK((g_last.flags & MLA_VERIFY_FLAG_CONTIGUOUS_PREFIX) != 0);
+    cf.flags = 0x100;
+    CHECK(mla_verify_plan(&cf, &pf) == MLA_VERIFY_ERR_INVALID_ARGUMENT);
+  }
   const float* ref = (const float*)((uintptr_t)1 << 42);
   CHECK(mla_verify_compare(&plan, &a, ref, 8 * 512, 512, nullptr, 0, wsp, ws, nullptr) == MLA_VERIFY_OK);
   CHECK(mla_verify_compare(&plan, &a, ref, 8 * 512, 510, nullptr, 0, wsp, ws, nullptr) ==
